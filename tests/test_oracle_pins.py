@@ -1,0 +1,258 @@
+"""Pins of the fp64 oracle against facts other than itself.
+
+* central finite differences of its own forward (pins every backward term);
+* closed forms of special cases: frozen state (g = 0, beta = 0), causal linear attention
+  (orthonormal keys, g = 0, h0 = 0), pure decay (beta = 0), each differentiated by torch
+  autograd in fp64 (an independent derivative), and the beta-tangent at beta = 0;
+* a two-token scalar example worked by hand from S_t = (1 - b k^2) e^g S_{t-1} + b k v;
+* the chunkwise form equals the token recurrence;
+* invariants: grouped heads equal replicated heads, packed sequences equal separate
+  runs, gradients are linear in (dO, dS_final).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.chunked import chunked_fwd_bwd
+
+GRADS = ["dq", "dk", "dv", "dg", "dbeta", "dh0"]
+
+
+def rand_inputs(rng, T, H, HV, K, V, N, h0=True, dsf=True, g_zero=False, beta_zero=False):
+    q = rng.standard_normal((T, H, K))
+    k = rng.standard_normal((T, H, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, HV, V))
+    g = np.zeros((T, HV, K)) if g_zero else -np.log1p(np.exp(-(rng.standard_normal((T, HV, K)) + 3.0)))
+    beta = np.zeros((T, HV)) if beta_zero else 1.0 / (1.0 + np.exp(-rng.standard_normal((T, HV))))
+    return dict(q=q, k=k, v=v, g=g, beta=beta,
+                h0=0.3 * rng.standard_normal((N, HV, K, V)) if h0 else None,
+                dS_final=0.3 * rng.standard_normal((N, HV, K, V)) if dsf else None,
+                dO=rng.standard_normal((T, HV, V)))
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def run(oracle_mod, x, cu, scale, backward=True):
+    return oracle_mod.run(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, scale, h0=x["h0"], dO=x["dO"],
+                          dS_final=x["dS_final"], backward=backward)
+
+
+@pytest.mark.parametrize("case", ["dense", "gva", "varlen"])
+def test_finite_differences(oracle_mod, case):
+    rng = np.random.default_rng({"dense": 11, "gva": 12, "varlen": 13}[case])
+    T, K, V = 8, 4, 4
+    H, HV = (1, 2) if case == "gva" else (1, 1)
+    cu = [0, 3, 8] if case == "varlen" else [0, 8]
+    N = len(cu) - 1
+    x = rand_inputs(rng, T, H, HV, K, V, N)
+    scale = K ** -0.5
+    ref = run(oracle_mod, x, cu, scale)
+    eps = 1e-6
+
+    def L(y):
+        return oracle_mod.loss(run(oracle_mod, y, cu, scale, backward=False), x["dO"], x["dS_final"])
+
+    for name, gname in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"), ("h0", "dh0")]:
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            y = dict(x)
+            y[name] = x[name].copy()
+            y[name][idx] += eps
+            lp = L(y)
+            y[name][idx] -= 2 * eps
+            lm = L(y)
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert rel(ref[gname], fd) < 1e-7, (case, gname, rel(ref[gname], fd))
+
+
+def test_hand_worked_scalar_example(oracle_mod):
+    # K = V = 1, scale = 1, h0 = 1. Token 1: k=1, beta=0.5, g=ln 0.5, v=2, q=1.
+    # Token 2: k=1, beta=0.25, g=0, v=-1, q=2. dO = (1, 1), no dS_final.
+    # S1 = (1-0.5)(0.5)(1) + 0.5*2 = 1.25 ; S2 = (1-0.25)(1)(1.25) + 0.25*(-1) = 0.6875
+    # o = (1.25, 1.375); L = o1 + o2; dS2/dS1 = 0.75, dL/dS1 = 1 + 2*0.75 = 2.5
+    # dv1 = 2.5*0.5 = 1.25 ; dv2 = 2*0.25 = 0.5
+    # dbeta1 = 2.5*(-0.5 + 2) = 3.75 ; dbeta2 = 2*(-1.25 - 1) = -4.5
+    # dq1 = S1 = 1.25 ; dq2 = S2 = 0.6875
+    # dg1 = 2.5*(0.5*0.5) = 0.625 ; dg2 = 2*(0.75*1.25) = 1.875 ; dh0 = 2.5*0.25 = 0.625
+    # dk1 = 2.5*(-2*0.5*1*0.5 + 0.5*2) = 1.25 ; dk2 = 2*(-2*0.25*1.25 + 0.25*(-1)) = -1.75
+    c = lambda *a: np.array(a, dtype=np.float64)
+    q = c(1.0, 2.0).reshape(2, 1, 1)
+    k = c(1.0, 1.0).reshape(2, 1, 1)
+    v = c(2.0, -1.0).reshape(2, 1, 1)
+    g = c(np.log(0.5), 0.0).reshape(2, 1, 1)
+    beta = c(0.5, 0.25).reshape(2, 1)
+    h0 = c(1.0).reshape(1, 1, 1, 1)
+    dO = c(1.0, 1.0).reshape(2, 1, 1)
+    r = oracle_mod.run(q, k, v, g, beta, [0, 2], 1.0, h0=h0, dO=dO)
+    np.testing.assert_allclose(r["o"].ravel(), [1.25, 1.375], rtol=1e-14)
+    np.testing.assert_allclose(r["S_T"].ravel(), [0.6875], rtol=1e-14)
+    np.testing.assert_allclose(r["dv"].ravel(), [1.25, 0.5], rtol=1e-14)
+    np.testing.assert_allclose(r["dbeta"].ravel(), [3.75, -4.5], rtol=1e-14)
+    np.testing.assert_allclose(r["dq"].ravel(), [1.25, 0.6875], rtol=1e-14)
+    np.testing.assert_allclose(r["dg"].ravel(), [0.625, 1.875], rtol=1e-14)
+    np.testing.assert_allclose(r["dh0"].ravel(), [0.625], rtol=1e-14)
+    np.testing.assert_allclose(r["dk"].ravel(), [1.25, -1.75], rtol=1e-14)
+
+
+def test_frozen_state_g0_beta0(oracle_mod):
+    """g = 0 and beta = 0: S_t = h0 for all t, so o_t = scale h0^T q_t. With
+    P_t = dS_final + scale sum_{s>=t} q_s dO_s^T: dq_t = scale h0 dO_t, dk = dv = 0,
+    dh0 = P_0, dg_t = rowsum(P_t o h0), dbeta_t = k_t^T P_t (v_t - h0^T k_t)."""
+    rng = np.random.default_rng(21)
+    T, K, V = 12, 5, 3
+    x = rand_inputs(rng, T, 1, 1, K, V, 1, g_zero=True, beta_zero=True)
+    scale = 0.7
+    r = run(oracle_mod, x, [0, T], scale)
+    q, k, v, h0, dO, dSf = x["q"][:, 0], x["k"][:, 0], x["v"][:, 0], x["h0"][0, 0], x["dO"][:, 0], x["dS_final"][0, 0]
+    np.testing.assert_allclose(r["o"][:, 0], scale * q @ h0, rtol=1e-12, atol=1e-12)
+    outer = scale * np.einsum("tk,tv->tkv", q, dO)
+    P = dSf[None] + np.cumsum(outer[::-1], axis=0)[::-1]
+    np.testing.assert_allclose(r["dq"][:, 0], scale * dO @ h0.T, rtol=1e-12, atol=1e-12)
+    assert np.abs(r["dk"]).max() == 0 and np.abs(r["dv"]).max() == 0
+    np.testing.assert_allclose(r["dh0"][0, 0], P[0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["dg"][:, 0], np.einsum("tkv,kv->tk", P, h0), rtol=1e-12, atol=1e-12)
+    resid = v - k @ h0
+    np.testing.assert_allclose(r["dbeta"][:, 0], np.einsum("tk,tkv,tv->t", k, P, resid), rtol=1e-12, atol=1e-12)
+
+
+def test_orthonormal_keys_is_causal_linear_attention(oracle_mod):
+    """g = 0, h0 = 0, keys orthonormal: every residual equals v, so
+    o_t = scale sum_{s<=t} beta_s (q_t . k_s) v_s and S_T = sum_s beta_s k_s v_s^T.
+    dq, dv, dbeta are then linear attention's gradients (torch autograd, fp64)."""
+    rng = np.random.default_rng(31)
+    T, K, V = 7, 8, 5
+    x = rand_inputs(rng, T, 1, 1, K, V, 1, h0=False, g_zero=True)
+    Qm, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    x["k"] = np.ascontiguousarray(Qm[:T][:, None, :])
+    scale = K ** -0.5
+    r = run(oracle_mod, x, [0, T], scale)
+    q = torch.tensor(x["q"][:, 0], requires_grad=True)
+    k = torch.tensor(x["k"][:, 0])
+    v = torch.tensor(x["v"][:, 0], requires_grad=True)
+    b = torch.tensor(x["beta"][:, 0], requires_grad=True)
+    A = torch.tril(q @ k.T) * b[None, :] * scale
+    o = A @ v
+    ST = (k * b[:, None]).T @ v
+    L = (o * torch.tensor(x["dO"][:, 0])).sum() + (ST * torch.tensor(x["dS_final"][0, 0])).sum()
+    L.backward()
+    np.testing.assert_allclose(r["o"][:, 0], o.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["S_T"][0, 0], ST.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["dq"][:, 0], q.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["dv"][:, 0], v.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["dbeta"][:, 0], b.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_beta_zero_pure_decay(oracle_mod):
+    """beta = 0: S_t = Diag(exp(Gs_t)) h0 with Gs the sequence-level cumsum of g. o, S_T
+    and dq, dg, dh0 follow by torch autograd of that closed form; dk = dv = 0. dbeta is the
+    tangent of the model with independent first-order writes
+    S_s = Diag(e^{Gs_s}) h0 + sum_{t<=s} beta_t Diag(e^{Gs_s - Gs_t}) k_t r_t^T,
+    r_t = v_t - (Diag(e^{Gs_t}) h0)^T k_t, which agrees with KDA to first order in beta."""
+    rng = np.random.default_rng(41)
+    T, K, V = 9, 4, 3
+    x = rand_inputs(rng, T, 1, 1, K, V, 1, beta_zero=True)
+    scale = 0.5
+    r = run(oracle_mod, x, [0, T], scale)
+    q = torch.tensor(x["q"][:, 0], requires_grad=True)
+    g = torch.tensor(x["g"][:, 0], requires_grad=True)
+    h0 = torch.tensor(x["h0"][0, 0], requires_grad=True)
+    b = torch.zeros(T, dtype=torch.float64, requires_grad=True)
+    k = torch.tensor(x["k"][:, 0])
+    v = torch.tensor(x["v"][:, 0])
+    dO = torch.tensor(x["dO"][:, 0])
+    dSf = torch.tensor(x["dS_final"][0, 0])
+    Gs = torch.cumsum(g, 0)
+    S = torch.exp(Gs)[:, :, None] * h0[None]                        # [T, K, V]
+    resid = v - torch.einsum("tkv,tk->tv", S, k)                    # r_t at beta = 0
+    D = torch.exp(Gs[:, None, :] - Gs[None, :, :])                  # [s, t, K]
+    causal = torch.tril(torch.ones(T, T, dtype=torch.float64))[:, :, None]
+    S1 = S + torch.einsum("st,stk,tk,tv->skv", causal[:, :, 0] * b[None, :], D, k, resid)
+    o = scale * torch.einsum("skv,sk->sv", S1, q)
+    L = (o * dO).sum() + (S1[-1] * dSf).sum()
+    L.backward()
+    np.testing.assert_allclose(r["o"][:, 0], o.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["S_T"][0, 0], S1[-1].detach().numpy(), rtol=1e-12, atol=1e-12)
+    for key, ref in [("dq", q.grad), ("dg", g.grad), ("dbeta", b.grad)]:
+        np.testing.assert_allclose(r[key][:, 0], ref.numpy(), rtol=1e-10, atol=1e-12, err_msg=key)
+    np.testing.assert_allclose(r["dh0"][0, 0], h0.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.abs(r["dk"]).max() == 0 and np.abs(r["dv"]).max() == 0
+
+
+@pytest.mark.parametrize("C", [4, 16, 64])
+def test_chunked_equals_recurrent(oracle_mod, C):
+    rng = np.random.default_rng(50 + C)
+    T, H, HV, K, V = 75, 1, 2, 8, 6
+    cu = [0, 29, 75]
+    x = rand_inputs(rng, T, H, HV, K, V, 2)
+    scale = K ** -0.5
+    ref = run(oracle_mod, x, cu, scale)
+    ch = chunked_fwd_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, scale, C, h0=x["h0"], dO=x["dO"],
+                         dS_final=x["dS_final"])
+    for key in ["o", "S_T"] + GRADS:
+        assert rel(ch[key], ref[key]) < 1e-10, (C, key, rel(ch[key], ref[key]))
+
+
+def test_gva_equals_replicated_heads(oracle_mod):
+    rng = np.random.default_rng(61)
+    T, H, HV, K, V = 10, 2, 6, 4, 3
+    x = rand_inputs(rng, T, H, HV, K, V, 1)
+    scale = 0.4
+    ref = run(oracle_mod, x, [0, T], scale)
+    Gs = HV // H
+    y = dict(x)
+    y["q"] = np.ascontiguousarray(np.repeat(x["q"], Gs, axis=1))
+    y["k"] = np.ascontiguousarray(np.repeat(x["k"], Gs, axis=1))
+    exp = run(oracle_mod, y, [0, T], scale)
+    for key in ["o", "S_T", "dv", "dg", "dbeta", "dh0"]:
+        np.testing.assert_allclose(ref[key], exp[key], rtol=1e-13, atol=1e-14)
+    for key in ["dq", "dk"]:
+        np.testing.assert_allclose(ref[key], exp[key].reshape(T, H, Gs, K).sum(axis=2), rtol=1e-12, atol=1e-14)
+
+
+def test_varlen_equals_separate_runs(oracle_mod):
+    rng = np.random.default_rng(71)
+    cu = [0, 5, 6, 19]
+    T, K, V = 19, 4, 4
+    x = rand_inputs(rng, T, 1, 1, K, V, 3)
+    scale = 0.5
+    ref = run(oracle_mod, x, cu, scale)
+    for n in range(3):
+        sl = slice(cu[n], cu[n + 1])
+        y = {key: (val[sl] if key in ("q", "k", "v", "g", "beta", "dO") else val[n:n + 1]) for key, val in x.items()}
+        y = {key: np.ascontiguousarray(val) for key, val in y.items()}
+        one = run(oracle_mod, y, [0, cu[n + 1] - cu[n]], scale)
+        for key in ["o", "dq", "dk", "dv", "dg", "dbeta"]:
+            np.testing.assert_allclose(ref[key][sl], one[key], rtol=1e-14, atol=1e-15)
+        for key in ["S_T", "dh0"]:
+            np.testing.assert_allclose(ref[key][n:n + 1], one[key], rtol=1e-14, atol=1e-15)
+
+
+def test_gradients_linear_in_cotangents(oracle_mod):
+    rng = np.random.default_rng(81)
+    T, K, V = 11, 4, 5
+    x = rand_inputs(rng, T, 1, 1, K, V, 1)
+    y = dict(x)
+    y["dO"] = rng.standard_normal(x["dO"].shape)
+    y["dS_final"] = rng.standard_normal(x["dS_final"].shape)
+    z = dict(x)
+    z["dO"] = 2.0 * x["dO"] - 3.0 * y["dO"]
+    z["dS_final"] = 2.0 * x["dS_final"] - 3.0 * y["dS_final"]
+    a, b, c = (run(oracle_mod, w, [0, T], 0.5) for w in (x, y, z))
+    for key in GRADS:
+        np.testing.assert_allclose(c[key], 2.0 * a[key] - 3.0 * b[key], rtol=1e-11, atol=1e-12)
+
+
+def test_thread_count_does_not_change_bits(oracle_mod):
+    rng = np.random.default_rng(91)
+    T, H, HV, K, V = 20, 1, 4, 4, 4
+    x = rand_inputs(rng, T, H, HV, K, V, 1)
+    a = oracle_mod.run(x["q"], x["k"], x["v"], x["g"], x["beta"], [0, T], 0.5, h0=x["h0"], dO=x["dO"],
+                       dS_final=x["dS_final"], nthreads=1)
+    b = oracle_mod.run(x["q"], x["k"], x["v"], x["g"], x["beta"], [0, T], 0.5, h0=x["h0"], dO=x["dO"],
+                       dS_final=x["dS_final"], nthreads=4)
+    for key in ["o", "S_T"] + GRADS:
+        assert np.array_equal(a[key], b[key]), key
