@@ -1,0 +1,654 @@
+// Backward chunk kernels of KDA for gfx950.
+//
+// Chunk algebra of the backward (FlashKDA backward page, steps 1-3 and the dMqk / dqd /
+// dki / dkd / dbeta products; FLA chunk_kda_bwd page, kernels dAv and wy_dqkg_fused, the
+// intra-chunk step, the GVA reduction and the reverse chunk-local cumsum of dg). With
+// dS the gradient w.r.t. a chunk's S_out:
+//   dU = Mqk^T dO + kr dS;  dvc = INV^T dU;  dv = diag(beta) dvc
+//   dS_in = diag(e^gam) dS + qd^T dO - kd^T diag(beta) dvc
+//   dMqk = tril(dO U^T);  dL = -strict_tril(dvc U^T)
+//   dqd = dO S_in^T + dMqk ki;  dkd = diag(beta)(dL ki - dvc S_in^T)
+//   dki = dMqk^T qd + (diag(beta) dL)^T kd;  dkr = U dS^T
+//   dbeta = rowsum(dvc o (v - kd S_in)) + rowsum(kd o (dL ki))
+//   dq = scale e^G dqd;  dk = e^G dkd + e^-G dki + e^(gam-G) dkr
+//   dG = q o dq + k o (e^G dkd - e^-G dki - e^(gam-G) dkr)
+//   dG[last] += e^gam o rowsum(dS o S_in) + sum_j kr_j o dkr_j;  dg = reverse cumsum of dG.
+//
+// bwd_prep_kernel writes what the reverse scan needs per chunk (kr, -w^T, e^gam and
+// W = (qd - Mqk w)^T dO, so that dS_in = diag(e^gam) dS + W - w^T (kr dS)); the scan then
+// leaves dS and kr dS per chunk; bwd_grad_kernel forms every gradient of one chunk with
+// all C x C triangles kept in LDS.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <class T, int K, int V, int C>
+struct BwdPrepLds {
+  static constexpr int P = pad_of<T>();
+  static constexpr int LDK = K + P, LDC = C + P;
+  static constexpr size_t oQd = 0;
+  static constexpr size_t oKi = oQd + sizeof(T) * C * LDK;
+  static constexpr size_t oBKdT = oKi + sizeof(T) * C * LDK;
+  static constexpr size_t oDoT = oBKdT + sizeof(T) * K * LDC;
+  static constexpr size_t oINV = oDoT + sizeof(T) * V * LDC;
+  static constexpr size_t oMqk = oINV + sizeof(T) * C * LDC;
+  static constexpr size_t oWT = oMqk + sizeof(T) * C * LDC;
+  static constexpr size_t oQpT = oWT + sizeof(T) * K * LDC;
+  static constexpr size_t oBeta = oQpT + sizeof(T) * K * LDC;
+  static constexpr size_t total = oBeta + sizeof(float) * C;
+};
+
+// One workgroup per (chunk, value head).
+template <class T, int K, int V, int C>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
+                                                        const float* __restrict__ gp, const float* __restrict__ bp,
+                                                        const T* __restrict__ invp, const T* __restrict__ dOp,
+                                                        BwdWs ws) {
+  typedef BwdPrepLds<T, K, V, C> Lay;
+  constexpr int NW = 4, RT = C / 16, KT = K / 16, VT = V / 16;
+  constexpr int LDK = Lay::LDK, LDC = Lay::LDC;
+  __shared__ __align__(16) unsigned char smem[Lay::total];
+  T* Qd = reinterpret_cast<T*>(smem + Lay::oQd);
+  T* Ki = reinterpret_cast<T*>(smem + Lay::oKi);
+  T* BKdT = reinterpret_cast<T*>(smem + Lay::oBKdT);
+  T* DoT = reinterpret_cast<T*>(smem + Lay::oDoT);
+  T* INVt = reinterpret_cast<T*>(smem + Lay::oINV);
+  T* Mqk = reinterpret_cast<T*>(smem + Lay::oMqk);
+  T* WT = reinterpret_cast<T*>(smem + Lay::oWT);
+  T* QpT = reinterpret_cast<T*>(smem + Lay::oQpT);
+  float* betas = reinterpret_cast<float*>(smem + Lay::oBeta);
+
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int hq = h / (s.HV / s.H);
+  const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, grp = lane >> 4;
+  const long ch = (long)c * s.HV + h;
+  const int len = geo.len;
+  if (len <= 0) return;
+  const int qs = s.H * K, gs = s.HV * K, vs = s.HV * V;
+  const T* qc = qp + (geo.bos * s.H + hq) * K;
+  const T* kc = kp + (geo.bos * s.H + hq) * K;
+  const float* gc = gp + (geo.bos * s.HV + h) * K;
+  const T* dOc = dOp + (geo.bos * s.HV + h) * V;
+  const float* bc = bp + geo.bos * s.HV + h;
+
+  if (tid < C) betas[tid] = tid < len ? bc[tid * s.HV] : 0.f;
+  __syncthreads();
+
+  T* krg = reinterpret_cast<T*>(ws.kr) + ch * C * K;
+  for (int kt = wave; kt < KT; kt += NW) {
+    const int col = 16 * kt + n;
+    float G[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * rt + 4 * grp + j;
+        G[rt][j] = row < len ? gc[row * gs + col] : 0.f;
+      }
+    col_prefix<RT>(G, lane);
+    const float gam = __shfl(G[RT - 1][3], n + 48, 64);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 bk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * rt + 4 * grp + j;
+        const int off = row * qs + col;
+        const float kv = row < len ? to_f(kc[off]) : 0.f;
+        const float qv = row < len ? to_f(qc[off]) : 0.f;
+        const float e = __expf(G[rt][j]);
+        Qd[row * LDK + col] = from_f<T>(s.scale * qv * e);
+        Ki[row * LDK + col] = from_f<T>(kv * __expf(-G[rt][j]));
+        bk[j] = betas[row] * kv * e;
+        krg[row * K + col] = from_f<T>(kv * __expf(gam - G[rt][j]));
+      }
+      st4(BKdT + col * LDC + 16 * rt + 4 * grp, bk);
+    }
+    if (grp == 0) ws.eg[ch * K + col] = __expf(gam);
+  }
+  for (int vt = wave; vt < VT; vt += NW) {
+    const int col = 16 * vt + n;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 d4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * rt + 4 * grp + j;
+        d4[j] = row < len ? to_f(dOc[row * vs + col]) : 0.f;
+      }
+      st4(DoT + col * LDC + 16 * rt + 4 * grp, d4);
+    }
+  }
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int i = idx / C, j = idx % C;
+    const float val = (i < len && j < len) ? to_f(invp[ch * C * C + idx]) : (i == j ? 1.f : 0.f);
+    INVt[i * LDC + j] = from_f<T>(val);
+  }
+  __syncthreads();
+
+  // Mqk = tril(qd ki^T), row-major.
+  block_gemm<T, RT, RT, 1, NW, K>(
+      Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
+      [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
+          Mqk[row * LDC + col] = from_f<T>(col <= row ? acc[0][j] : 0.f);
+        }
+      }, wave, lane);
+  // w = INV diag(beta) kd: kept transposed in LDS, stored negated and transposed for the scan.
+  T* nwT = reinterpret_cast<T*>(ws.nwT) + ch * K * C;
+  constexpr int BNK = KT % 2 == 0 ? 2 : 1;
+  block_gemm<T, RT, KT, BNK, NW, C>(
+      INVt, LDC, 1 << 30, BKdT, LDC, [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
+      [&](int, int mt, int nt0, f32x4(&acc)[BNK]) {
+#pragma unroll
+        for (int jb = 0; jb < BNK; ++jb) {
+          const int col = 16 * (nt0 + jb) + n;
+          st4(WT + col * LDC + 16 * mt + 4 * grp, acc[jb]);
+          st4(nwT + col * C + 16 * mt + 4 * grp, -acc[jb]);
+        }
+      }, wave, lane);
+  __syncthreads();
+  // Q' = qd - Mqk w, transposed.
+  block_gemm<T, RT, KT, BNK, NW, C>(
+      Mqk, LDC, 1 << 30, WT, LDC, [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
+      [&](int, int mt, int nt0, f32x4(&acc)[BNK]) {
+#pragma unroll
+        for (int jb = 0; jb < BNK; ++jb) {
+          const int col = 16 * (nt0 + jb) + n;
+          f32x4 qp4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qp4[j] = to_f(Qd[(16 * mt + 4 * grp + j) * LDK + col]) - acc[jb][j];
+          st4(QpT + col * LDC + 16 * mt + 4 * grp, qp4);
+        }
+      }, wave, lane);
+  __syncthreads();
+  // W = Q'^T dO, stored transposed [V][K].
+  T* bcT = reinterpret_cast<T*>(ws.bcT) + ch * V * K;
+  constexpr int BNV = VT % 2 == 0 ? 2 : 1;
+  block_gemm<T, KT, VT, BNV, NW, C>(QpT, LDC, 1 << 30, DoT, LDC, FullRange(),
+                                    [&](int, int mt, int nt0, f32x4(&acc)[BNV]) {
+#pragma unroll
+                                      for (int jb = 0; jb < BNV; ++jb)
+                                        st4(bcT + (16 * (nt0 + jb) + n) * K + 16 * mt + 4 * grp, acc[jb]);
+                                    }, wave, lane);
+}
+
+// LDS plan of the gradient kernel. Phase-2 temporaries alias buffers that are written
+// later; every alias is separated from its predecessor's last read by a barrier.
+//   region A [0, endA): Qd, Kd, Ki, S_in^T (phase 1-2)  |  Qd^T, Kd^T, Ki^T, U, -dvc (phase 2-3)
+//   region B [endA, endB): vcorr^T then dU^T, INV, INV^T  |  dMqk, dMqk^T, dL, (beta dL)^T
+//   then Mqk^T, beta, dbeta partials, dO^T
+template <class T, int K, int V, int C>
+struct GradLds {
+  static constexpr int NW = 8;
+  static constexpr int P = pad_of<T>();
+  static constexpr int LDK = K + P, LDC = C + P, LDV = V + P;
+  static constexpr size_t szCK = sizeof(T) * C * LDK, szKC = sizeof(T) * K * LDC, szCV = sizeof(T) * C * LDV;
+  static constexpr size_t szVC = sizeof(T) * V * LDC, szVK = sizeof(T) * V * LDK, szCC = sizeof(T) * C * LDC;
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t oQd = 0, oKd = szCK, oKi = 2 * szCK, oSinT = 3 * szCK;
+  static constexpr size_t oQdT = 0, oKdT = szKC, oKiT = 2 * szKC, oU = 3 * szKC, oNdv = 3 * szKC + szCV;
+  static constexpr size_t endA = mx(3 * szCK + szVK, 3 * szKC + 2 * szCV);
+  static constexpr size_t oVcT = endA, oDuT = endA;
+  static constexpr size_t oINV = endA + szVC, oINVT = oINV + szCC;
+  static constexpr size_t oDMqk = endA, oDMqkT = endA + szCC, oDL = endA + 2 * szCC, oBDLT = endA + 3 * szCC;
+  static constexpr size_t endB = mx(endA + szVC + 2 * szCC, endA + 4 * szCC);
+  static constexpr size_t oMqkT = endB;
+  static constexpr size_t oBeta = oMqkT + szCC;
+  static constexpr size_t oDbp = oBeta + sizeof(float) * C;
+  static constexpr size_t oDoT = oDbp + sizeof(float) * NW * C;
+  static constexpr size_t total = oDoT + szVC;
+  static_assert(total <= 160 * 1024, "gradient kernel exceeds the LDS of one CU");
+};
+
+// One workgroup per (chunk, q/k head); the value heads of the group are processed in
+// turn and their dq, dk contributions summed in registers.
+template <class T, int K, int V, int C>
+__global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
+                                                        const T* __restrict__ vp, const float* __restrict__ gp,
+                                                        const float* __restrict__ bp, const T* __restrict__ states,
+                                                        const T* __restrict__ invp, const T* __restrict__ dOp,
+                                                        BwdWs ws, T* __restrict__ dqp, T* __restrict__ dkp,
+                                                        T* __restrict__ dvp, float* __restrict__ dgp,
+                                                        float* __restrict__ dbp) {
+  typedef GradLds<T, K, V, C> Lay;
+  typedef Mma<T> M;
+  constexpr int NW = Lay::NW, RT = C / 16, KT = K / 16, VT = V / 16;
+  constexpr int NCT = (KT + NW - 1) / NW;
+  constexpr int LDK = Lay::LDK, LDC = Lay::LDC, LDV = Lay::LDV;
+  constexpr int BN1 = VT % 2 == 0 ? 2 : 1;
+  constexpr int NIT1 = (RT * (VT / BN1) + NW - 1) / NW;
+  __shared__ __align__(16) unsigned char smem[Lay::total];
+  T* Qd = reinterpret_cast<T*>(smem + Lay::oQd);
+  T* Kd = reinterpret_cast<T*>(smem + Lay::oKd);
+  T* Ki = reinterpret_cast<T*>(smem + Lay::oKi);
+  T* SinT = reinterpret_cast<T*>(smem + Lay::oSinT);
+  T* QdT = reinterpret_cast<T*>(smem + Lay::oQdT);
+  T* KdT = reinterpret_cast<T*>(smem + Lay::oKdT);
+  T* KiT = reinterpret_cast<T*>(smem + Lay::oKiT);
+  T* U = reinterpret_cast<T*>(smem + Lay::oU);
+  T* Ndv = reinterpret_cast<T*>(smem + Lay::oNdv);
+  T* VcT = reinterpret_cast<T*>(smem + Lay::oVcT);
+  T* DuT = reinterpret_cast<T*>(smem + Lay::oDuT);
+  T* INVt = reinterpret_cast<T*>(smem + Lay::oINV);
+  T* INVTt = reinterpret_cast<T*>(smem + Lay::oINVT);
+  T* DMqk = reinterpret_cast<T*>(smem + Lay::oDMqk);
+  T* DMqkT = reinterpret_cast<T*>(smem + Lay::oDMqkT);
+  T* DL = reinterpret_cast<T*>(smem + Lay::oDL);
+  T* BDLT = reinterpret_cast<T*>(smem + Lay::oBDLT);
+  T* MqkT = reinterpret_cast<T*>(smem + Lay::oMqkT);
+  float* betas = reinterpret_cast<float*>(smem + Lay::oBeta);
+  float* dbpart = reinterpret_cast<float*>(smem + Lay::oDbp);
+  T* DoT = reinterpret_cast<T*>(smem + Lay::oDoT);
+
+  const int c = blockIdx.x, hq = blockIdx.y;
+  const int Gq = s.HV / s.H;
+  const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, grp = lane >> 4;
+  const int len = geo.len;
+  const long bos = geo.bos;
+  if (len <= 0) return;
+  const int qs = s.H * K, gs = s.HV * K, vs = s.HV * V;
+  const T* qc = qp + (bos * s.H + hq) * K;
+  const T* kc = kp + (bos * s.H + hq) * K;
+
+  float dqa[NCT][RT][4], dka[NCT][RT][4];
+#pragma unroll
+  for (int ci = 0; ci < NCT; ++ci)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dqa[ci][rt][j] = dka[ci][rt][j] = 0.f;
+
+  for (int e = 0; e < Gq; ++e) {
+    const int h = hq * Gq + e;
+    // Per-iteration opaque copies: keep lane-dependent addresses and row masks from being
+    // hoisted out of this loop (which would hold hundreds of them live across its body).
+    const int tid = opaque_v(threadIdx.x);
+    const int lane = tid & 63, n = lane & 15, grp = lane >> 4;
+    const int wave = opaque_s(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    const int len = opaque_s(__builtin_amdgcn_readfirstlane(geo.len));
+    const long ch = (long)c * s.HV + h;
+    const T* Sin = states + ch * K * V;
+    const T* dSo = reinterpret_cast<const T*>(ws.dS) + ch * K * V;
+    const T* dOc = dOp + (bos * s.HV + h) * V;  // row stride HV*V
+    const T* vc = vp + (bos * s.HV + h) * V;
+    const float* gc = gp + (bos * s.HV + h) * K;
+    const float* bc = bp + bos * s.HV + h;
+    T* dvc_out = dvp + (bos * s.HV + h) * V;
+    float* dgc = dgp + (bos * s.HV + h) * K;
+    float* dbc = dbp + bos * s.HV + h;
+
+    if (tid < C) betas[tid] = tid < len ? bc[tid * s.HV] : 0.f;
+    for (int i = tid; i < NW * C; i += 64 * NW) dbpart[i] = 0.f;
+
+    // ---- phase 1: gate cumsum (kept in registers), qd, kd, ki; S_in^T; INV, INV^T
+    float Gr[NCT][RT][4], gam[NCT];
+#pragma unroll
+    for (int ci = 0; ci < NCT; ++ci) {
+      const int kt = wave + ci * NW;
+      gam[ci] = 0.f;
+      if (kt < KT) {
+        const int col = 16 * kt + n;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 16 * rt + 4 * grp + j;
+            Gr[ci][rt][j] = row < len ? gc[row * gs + col] : 0.f;
+          }
+        col_prefix<RT>(Gr[ci], lane);
+        gam[ci] = __shfl(Gr[ci][RT - 1][3], n + 48, 64);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 16 * rt + 4 * grp + j;
+            const int off = row * qs + col;
+            const float kv = row < len ? to_f(kc[off]) : 0.f;
+            const float qv = row < len ? to_f(qc[off]) : 0.f;
+            const float eG = __expf(Gr[ci][rt][j]);
+            Qd[row * LDK + col] = from_f<T>(s.scale * qv * eG);
+            Kd[row * LDK + col] = from_f<T>(kv * eG);
+            Ki[row * LDK + col] = from_f<T>(kv * __expf(-Gr[ci][rt][j]));
+          }
+      }
+    }
+    for (int vt = wave; vt < VT; vt += NW) {
+      const int col = 16 * vt + n;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        f32x4 s4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s4[j] = to_f(Sin[(16 * kt + 4 * grp + j) * V + col]);
+        st4(SinT + col * LDK + 16 * kt + 4 * grp, s4);
+      }
+    }
+    for (int idx = tid; idx < C * C; idx += 64 * NW) {
+      const int i = idx / C, j = idx % C;
+      const float val = (i < len && j < len) ? to_f(invp[ch * C * C + idx]) : (i == j ? 1.f : 0.f);
+      const T vt = from_f<T>(val);
+      INVt[i * LDC + j] = vt;
+      INVTt[j * LDC + i] = vt;
+    }
+    __syncthreads();
+
+    // ---- Mqk = tril(qd ki^T) -> Mqk^T
+    block_gemm<T, RT, RT, 1, NW, K>(
+        Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
+        [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+          f32x4 m4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) m4[j] = (16 * nt0 + n <= 16 * mt + 4 * grp + j) ? acc[0][j] : 0.f;
+          st4(MqkT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, m4);
+        }, wave, lane);
+    // ---- kd S_in -> vc0 = v - kd S_in (registers), vcorr^T = (beta vc0)^T
+    f32x4 vc0[NIT1][BN1];
+    block_gemm<T, RT, VT, BN1, NW, K>(Kd, LDK, 1 << 30, SinT, LDK, FullRange(),
+                                      [&](int it, int mt, int nt0, f32x4(&acc)[BN1]) {
+#pragma unroll
+                                        for (int jb = 0; jb < BN1; ++jb) {
+                                          const int col = 16 * (nt0 + jb) + n;
+                                          f32x4 r, b4;
+#pragma unroll
+                                          for (int j = 0; j < 4; ++j) {
+                                            const int row = 16 * mt + 4 * grp + j;
+                                            const float vv =
+                                                row < len ? to_f(vc[row * vs + col]) : 0.f;
+                                            r[j] = vv - acc[jb][j];
+                                            b4[j] = betas[row] * r[j];
+                                          }
+                                          vc0[it][jb] = r;
+                                          st4(VcT + col * LDC + 16 * mt + 4 * grp, b4);
+                                        }
+                                      }, wave, lane);
+    __syncthreads();
+
+    // ---- qd^T, kd^T, ki^T (region A, over the dead Qd/Kd/Ki/S_in^T)
+#pragma unroll
+    for (int ci = 0; ci < NCT; ++ci) {
+      const int kt = wave + ci * NW;
+      if (kt < KT) {
+        const int col = 16 * kt + n;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4 q4, kd4, ki4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 16 * rt + 4 * grp + j;
+            const int off = row * qs + col;
+            const float kv = row < len ? to_f(kc[off]) : 0.f;
+            const float qv = row < len ? to_f(qc[off]) : 0.f;
+            const float eG = __expf(Gr[ci][rt][j]);
+            q4[j] = s.scale * qv * eG;
+            kd4[j] = kv * eG;
+            ki4[j] = kv * __expf(-Gr[ci][rt][j]);
+          }
+          st4(QdT + col * LDC + 16 * rt + 4 * grp, q4);
+          st4(KdT + col * LDC + 16 * rt + 4 * grp, kd4);
+          st4(KiT + col * LDC + 16 * rt + 4 * grp, ki4);
+        }
+      }
+    }
+    // ---- U = INV vcorr (row-major)
+    block_gemm<T, RT, VT, BN1, NW, C>(
+        INVt, LDC, 1 << 30, VcT, LDC, [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
+        [&](int, int mt, int nt0, f32x4(&acc)[BN1]) {
+#pragma unroll
+          for (int jb = 0; jb < BN1; ++jb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) U[(16 * mt + 4 * grp + j) * LDV + 16 * (nt0 + jb) + n] = from_f<T>(acc[jb][j]);
+        }, wave, lane);
+    // ---- dO^T
+    for (int vt = wave; vt < VT; vt += NW) {
+      const int col = 16 * vt + n;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 d4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * rt + 4 * grp + j;
+          d4[j] = row < len ? to_f(dOc[row * vs + col]) : 0.f;
+        }
+        st4(DoT + col * LDC + 16 * rt + 4 * grp, d4);
+      }
+    }
+    __syncthreads();
+
+    // ---- dU = Mqk^T dO + kr dS -> dU^T
+    const T* yT = reinterpret_cast<const T*>(ws.yT) + ch * V * C;
+    block_gemm<T, RT, VT, BN1, NW, C>(
+        MqkT, LDC, 1 << 30, DoT, LDC, [](int mt, int, int& kb, int& ke) { kb = round_dn<T>(16 * mt); },
+        [&](int, int mt, int nt0, f32x4(&acc)[BN1]) {
+#pragma unroll
+          for (int jb = 0; jb < BN1; ++jb) {
+            const int col = 16 * (nt0 + jb) + n;
+            st4(DuT + col * LDC + 16 * mt + 4 * grp, acc[jb] + ld4f(yT + col * C + 16 * mt + 4 * grp));
+          }
+        }, wave, lane);
+    __syncthreads();
+
+    // ---- dvc = INV^T dU -> -dvc (row-major), dv, dbeta part 1
+    block_gemm<T, RT, VT, BN1, NW, C>(
+        INVTt, LDC, 1 << 30, DuT, LDC, [](int mt, int, int& kb, int& ke) { kb = round_dn<T>(16 * mt); },
+        [&](int it, int mt, int nt0, f32x4(&acc)[BN1]) {
+          float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jb = 0; jb < BN1; ++jb) {
+            const int col = 16 * (nt0 + jb) + n;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int row = 16 * mt + 4 * grp + j;
+              const float dvc = acc[jb][j];
+              Ndv[row * LDV + col] = from_f<T>(-dvc);
+              if (row < len) dvc_out[row * vs + col] = from_f<T>(betas[row] * dvc);
+              part[j] += dvc * vc0[it][jb][j];
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p = row_allsum16(part[j]);
+            if (n == 0) dbpart[wave * C + 16 * mt + 4 * grp + j] += p;
+          }
+        }, wave, lane);
+    __syncthreads();
+
+    // ---- dMqk = tril(dO U^T), dL = strict_tril(-dvc U^T); row-major and transposed copies
+    block_gemm<T, RT, RT, 1, NW, V>(
+        dOc, vs, len, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
+        [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+          f32x4 m4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
+            m4[j] = col <= row ? acc[0][j] : 0.f;
+            DMqk[row * LDC + col] = from_f<T>(m4[j]);
+          }
+          st4(DMqkT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, m4);
+        }, wave, lane);
+    block_gemm<T, RT, RT, 1, NW, V>(
+        Ndv, LDV, 1 << 30, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
+        [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+          f32x4 b4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
+            const float l = col < row ? acc[0][j] : 0.f;
+            DL[row * LDC + col] = from_f<T>(l);
+            b4[j] = betas[row] * l;
+          }
+          st4(BDLT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, b4);
+        }, wave, lane);
+    __syncthreads();
+
+    // ---- phase 3: per column tile of K, the C x K gradients of this value head
+#pragma unroll
+    for (int ci = 0; ci < NCT; ++ci) {
+      const int kt = wave + ci * NW;
+      if (kt < KT) {
+        const int col = 16 * kt + n;
+        f32x4 aq[RT], az[RT], av[RT], ai[RT], ar[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) aq[rt] = az[rt] = av[rt] = ai[rt] = ar[rt] = zero4();
+        float rsum = 0.f;  // this lane's share of sum_v dS[k][v] S_in[k][v], k = col
+#pragma unroll 1
+        for (int kk = 0; kk < V; kk += M::KS) {
+          const typename M::frag bs = frag_ld<T>(Sin, V, 16 * kt, kk, lane);
+          const typename M::frag bd = frag_ld<T>(dSo, V, 16 * kt, kk, lane);
+          if constexpr (M::PER == 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) rsum += (float)bs[i] * (float)bd[i];
+          } else {
+            rsum += bs * bd;
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            aq[rt] = M::mma(frag_ld<T>(dOc, vs, 16 * rt, kk, lane, V, len), bs, aq[rt]);
+            av[rt] = M::mma(frag_ld<T>(Ndv, LDV, 16 * rt, kk, lane), bs, av[rt]);
+            ar[rt] = M::mma(frag_ld<T>(U, LDV, 16 * rt, kk, lane), bd, ar[rt]);
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int klo = min(C, round_up<T>(16 * (rt + 1)));
+#pragma unroll 1
+          for (int kk = 0; kk < klo; kk += M::KS) {
+            const typename M::frag b = frag_ld<T>(KiT, LDC, 16 * kt, kk, lane, C, 1 << 30);
+            aq[rt] = M::mma(frag_ld<T>(DMqk, LDC, 16 * rt, kk, lane, C, 1 << 30), b, aq[rt]);
+            az[rt] = M::mma(frag_ld<T>(DL, LDC, 16 * rt, kk, lane, C, 1 << 30), b, az[rt]);
+          }
+#pragma unroll 1
+          for (int kk = round_dn<T>(16 * rt); kk < C; kk += M::KS) {
+            ai[rt] = M::mma(frag_ld<T>(DMqkT, LDC, 16 * rt, kk, lane, C, 1 << 30),
+                            frag_ld<T>(QdT, LDC, 16 * kt, kk, lane, C, 1 << 30), ai[rt]);
+            ai[rt] = M::mma(frag_ld<T>(BDLT, LDC, 16 * rt, kk, lane, C, 1 << 30),
+                            frag_ld<T>(KdT, LDC, 16 * kt, kk, lane, C, 1 << 30), ai[rt]);
+          }
+        }
+        rsum = col_allsum(rsum);
+        const float g_last = gam[ci];
+        float dG[RT][4];
+        float krd = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          float dbz[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 16 * rt + 4 * grp + j;
+            const int off = row * qs + col;
+            const float kv = row < len ? to_f(kc[off]) : 0.f;
+            const float qv = row < len ? to_f(qc[off]) : 0.f;
+            const float G = Gr[ci][rt][j];
+            const float eG = __expf(G), emG = __expf(-G), erG = __expf(g_last - G);
+            const float Z = az[rt][j];
+            const float dkd = betas[row] * (Z + av[rt][j]);
+            const float dq_e = s.scale * eG * aq[rt][j];
+            const float dk_d = eG * dkd, dk_i = emG * ai[rt][j], dk_r = erG * ar[rt][j];
+            dqa[ci][rt][j] += dq_e;
+            dka[ci][rt][j] += dk_d + dk_i + dk_r;
+            dG[rt][j] = qv * dq_e + kv * (dk_d - dk_i - dk_r);
+            krd += kv * dk_r;
+            dbz[j] = kv * eG * Z;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p = row_allsum16(dbz[j]);
+            if (n == 0) dbpart[wave * C + 16 * rt + 4 * grp + j] += p;
+          }
+        }
+        krd = col_allsum(krd);
+        // dgam enters at the chunk's last valid row
+        const int rl = len - 1;
+        if (grp == (rl & 15) >> 2) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (rt == (rl >> 4) && j == (rl & 3)) dG[rt][j] += __expf(g_last) * rsum + krd;
+        }
+        col_suffix<RT>(dG, lane);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 16 * rt + 4 * grp + j;
+            if (row < len) dgc[row * gs + col] = dG[rt][j];
+          }
+      }
+    }
+    __syncthreads();
+    if (tid < len) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc += dbpart[w * C + tid];
+      dbc[tid * s.HV] = acc;
+    }
+    __syncthreads();
+  }
+
+  T* dqc = dqp + (bos * s.H + hq) * K;
+  T* dkc = dkp + (bos * s.H + hq) * K;
+#pragma unroll
+  for (int ci = 0; ci < NCT; ++ci) {
+    const int kt = wave + ci * NW;
+    if (kt < KT) {
+      const int col = 16 * kt + n;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * rt + 4 * grp + j;
+          if (row < len) {
+            const int off = row * qs + col;
+            dqc[off] = from_f<T>(dqa[ci][rt][j]);
+            dkc[off] = from_f<T>(dka[ci][rt][j]);
+          }
+        }
+    }
+  }
+}
+
+template <class T, int K, int V, int C>
+static hipError_t bwd_prep_t(const Shape& s, const void* q, const void* k, const float* g, const float* beta,
+                             const void* inv, const void* dO, const BwdWs& ws, hipStream_t st) {
+  if (s.NT == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C>), dim3(s.NT, s.HV), dim3(256), 0, st, s,
+                     static_cast<const T*>(q), static_cast<const T*>(k), g, beta, static_cast<const T*>(inv),
+                     static_cast<const T*>(dO), ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(int dtype, int C, const Shape& s, const void* q, const void* k, const float* g,
+                           const float* beta, const void* inv, const void* dO, const BwdWs& ws, hipStream_t st) {
+  if (dtype == 0) return bwd_prep_t<float, 16, 16, 16>(s, q, k, g, beta, inv, dO, ws, st);
+  if (C == 64) return bwd_prep_t<bf16, 128, 128, 64>(s, q, k, g, beta, inv, dO, ws, st);
+  return bwd_prep_t<bf16, 128, 128, 16>(s, q, k, g, beta, inv, dO, ws, st);
+}
+
+template <class T, int K, int V, int C>
+static hipError_t bwd_grad_t(const Shape& s, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const void* states, const void* inv, const void* dO, const BwdWs& ws,
+                             void* dq, void* dk, void* dv, float* dg, float* dbeta, hipStream_t st) {
+  if (s.NT == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_grad_kernel<T, K, V, C>), dim3(s.NT, s.H), dim3(64 * GradLds<T, K, V, C>::NW), 0, st, s, static_cast<const T*>(q),
+                     static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<const T*>(states),
+                     static_cast<const T*>(inv), static_cast<const T*>(dO), ws, static_cast<T*>(dq),
+                     static_cast<T*>(dk), static_cast<T*>(dv), dg, dbeta);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_grad(int dtype, int C, const Shape& s, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const void* states, const void* inv, const void* dO,
+                           const BwdWs& ws, void* dq, void* dk, void* dv, float* dg, float* dbeta, hipStream_t st) {
+  if (dtype == 0) return bwd_grad_t<float, 16, 16, 16>(s, q, k, v, g, beta, states, inv, dO, ws, dq, dk, dv, dg,
+                                                       dbeta, st);
+  if (C == 64)
+    return bwd_grad_t<bf16, 128, 128, 64>(s, q, k, v, g, beta, states, inv, dO, ws, dq, dk, dv, dg, dbeta, st);
+  return bwd_grad_t<bf16, 128, 128, 16>(s, q, k, v, g, beta, states, inv, dO, ws, dq, dk, dv, dg, dbeta, st);
+}
+
+}  // namespace kda

@@ -1,0 +1,338 @@
+// Device-side building blocks shared by the KDA kernels (gfx950 / CDNA4).
+//
+// Matrix products use the 16x16 MFMA tiles: bf16 operands with fp32 accumulation
+// (v_mfma_f32_16x16x32_bf16) for the bf16 path and fp32 operands (v_mfma_f32_16x16x4_f32)
+// for the fp32 path. Both take, per lane l, row (l % 16) of A and column (l % 16) of B,
+// with the lane group l / 16 selecting a slice of the contraction index, and return a
+// 16x16 fp32 tile in which lane l holds rows 4*(l/16) + j (j = 0..3) of column l % 16.
+// Because A and B are indexed by the same (lane group, slot) pairs, any fixed assignment
+// of contraction indices to (lane group, slot) computes the same sum; the scan kernel
+// uses this to feed accumulator tiles straight back in as B operands.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+template <class T>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  static constexpr int KS = 32;   // contraction length of one instruction
+  static constexpr int PER = 8;   // contraction values per lane per operand
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag zero() {
+    frag z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+    return z;
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int KS = 4;
+  static constexpr int PER = 1;
+  typedef float frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag zero() { return 0.0f; }
+};
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+template <class T>
+__device__ __forceinline__ T from_f(float x) { return (T)x; }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Padding (elements) added to the contiguous dimension of LDS matrices: 16 bytes keeps
+// 16-byte fragment loads aligned and staggers rows across banks.
+template <class T>
+constexpr int pad_of() { return 16 / (int)sizeof(T); }
+
+// Fragment of a row-major matrix whose contraction index is contiguous: lane l reads
+// row r0 + l%16 and contraction indices k0 + PER*(l/16) .. + PER-1. Contraction indices
+// >= kmax and rows >= rmax read as zero (kmax must be a multiple of PER).
+// Offsets are 32-bit: bases are per-chunk (wave-uniform) pointers and a chunk spans far
+// fewer than 2^31 elements.
+template <class T>
+__device__ __forceinline__ typename Mma<T>::frag frag_ld(const T* base, int ld, int r0, int k0, int lane,
+                                                           int kmax, int rmax) {
+  const int r = r0 + (lane & 15);
+  const int kk = k0 + Mma<T>::PER * (lane >> 4);
+  if (kk >= kmax || r >= rmax) return Mma<T>::zero();
+  return *reinterpret_cast<const typename Mma<T>::frag*>(base + (r * ld + kk));
+}
+
+// Same without bounds (all indices known to be valid).
+template <class T>
+__device__ __forceinline__ typename Mma<T>::frag frag_ld(const T* base, int ld, int r0, int k0, int lane) {
+  const int r = r0 + (lane & 15);
+  const int kk = k0 + Mma<T>::PER * (lane >> 4);
+  return *reinterpret_cast<const typename Mma<T>::frag*>(base + (r * ld + kk));
+}
+
+// Loads 4 consecutive elements as fp32 (8 bytes for bf16, 16 for fp32).
+__device__ __forceinline__ f32x4 ld4f(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// Stores 4 fp32 values as 4 consecutive elements.
+__device__ __forceinline__ void st4(bf16* p, f32x4 v) {
+  bf16x4 o;
+  o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// Geometry of one chunk: sequence index, local chunk index, first token (flat), valid rows.
+struct Geo {
+  int n;
+  int lc;
+  int len;
+  long bos;
+};
+
+// Chunks are numbered sequence by sequence. Dense batches (cu == nullptr): every sequence
+// has T tokens and ceil(T/C) chunks. Packed batches: choff[n] is the first chunk of
+// sequence n (choff[N] = total chunks); empty sequences own no chunk.
+__device__ __forceinline__ Geo chunk_geo(int c, const int32_t* cu, const int32_t* choff, int N, int T, int C) {
+  Geo g;
+  if (cu == nullptr) {
+    const int ntper = (T + C - 1) / C;
+    g.n = c / ntper;
+    g.lc = c - g.n * ntper;
+    g.bos = (long)g.n * T + (long)g.lc * C;
+    g.len = min(C, T - g.lc * C);
+  } else {
+    int lo = 0, hi = N;  // largest n with choff[n] <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (choff[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    g.n = lo;
+    if (lo >= N) {  // chunk index past the table (host and device copies disagree): empty
+      g.lc = 0;
+      g.bos = 0;
+      g.len = 0;
+      return g;
+    }
+    g.lc = c - choff[lo];
+    g.bos = (long)cu[lo] + (long)g.lc * C;
+    g.len = min(C, (int)((long)cu[lo + 1] - g.bos));
+  }
+  return g;
+}
+
+// First chunk, chunk count and first token of sequence n.
+__device__ __forceinline__ void seq_range(int n, const int32_t* cu, const int32_t* choff, int T, int C,
+                                          int& c0, int& nc) {
+  if (cu == nullptr) {
+    const int ntper = (T + C - 1) / C;
+    c0 = n * ntper;
+    nc = ntper;
+  } else {
+    c0 = choff[n];
+    nc = choff[n + 1] - choff[n];
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Column-owner layout. A C x K chunk tensor is split into 16x16 tiles; wave w owns the
+// column tiles kt = w, w + NW, ...; inside a column tile lane l owns column
+// 16*kt + l%16 and rows 16*rt + 4*(l/16) + j for every row tile rt and j = 0..3, the
+// same places an MFMA accumulator tile holds. Per-column scans over the rows run as a
+// 4-element in-lane scan plus an exchange of block totals among the 4 lanes
+// (l%16, l%16 + 16, +32, +48) that share a column.
+// ---------------------------------------------------------------------------------
+
+// Inclusive prefix sum over rows of one column: x[rt][j] holds row 16*rt + 4*grp + j.
+template <int RT>
+__device__ __forceinline__ void col_prefix(float (&x)[RT][4], int lane) {
+  float tot[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    x[rt][1] += x[rt][0];
+    x[rt][2] += x[rt][1];
+    x[rt][3] += x[rt][2];
+    tot[rt] = x[rt][3];
+  }
+  const int n = lane & 15, grp = lane >> 4;
+  float carry = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float before = carry, all = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const float b = __shfl(tot[rt], n + 16 * gg, 64);
+      if (gg < grp) before += b;
+      all += b;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[rt][j] += before;
+    carry += all;
+  }
+}
+
+// Inclusive suffix (reverse) sum over rows of one column.
+template <int RT>
+__device__ __forceinline__ void col_suffix(float (&x)[RT][4], int lane) {
+  float tot[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    x[rt][2] += x[rt][3];
+    x[rt][1] += x[rt][2];
+    x[rt][0] += x[rt][1];
+    tot[rt] = x[rt][0];
+  }
+  const int n = lane & 15, grp = lane >> 4;
+  float carry = 0.f;
+#pragma unroll
+  for (int rt = RT - 1; rt >= 0; --rt) {
+    float after = carry, all = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const float b = __shfl(tot[rt], n + 16 * gg, 64);
+      if (gg > grp) after += b;
+      all += b;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[rt][j] += after;
+    carry += all;
+  }
+}
+
+// Sum over the 4 lanes that share a column (same l % 16).
+__device__ __forceinline__ float col_allsum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Sum over the 16 lanes of one lane group (same rows, the 16 columns of a tile).
+__device__ __forceinline__ float row_allsum16(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------------
+// Block-cooperative product D = A * B over LDS / global operands: A row-major with the
+// contraction index contiguous (lda), B given as its transpose Bt (ldb) with the
+// contraction contiguous. Output tiles are grouped in blocks of 1 x BN tiles that share
+// their A fragments; blocks are dealt to the NW waves round-robin. For each block,
+// krange(mt, nt0, kb, ke) narrows the contraction range (triangular operands), and
+// epi(it, mt, nt0, acc) consumes the BN accumulator tiles (it = the wave's block
+// counter, usable to index per-wave register arrays).
+// ---------------------------------------------------------------------------------
+template <class T, int MT, int NT, int BN, int NW, int KMAX, class KR, class EPI>
+__device__ __forceinline__ void block_gemm(const T* A, int lda, int arows, const T* Bt, int ldb, KR krange,
+                                           EPI epi, int wave, int lane) {
+  typedef Mma<T> M;
+  constexpr int NBN = NT / BN;
+  constexpr int NB = MT * NBN;
+  constexpr int NIT = (NB + NW - 1) / NW;
+  static_assert(NT % BN == 0, "BN must divide the tile columns");
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int blk = wave + it * NW;
+    if (blk < NB) {
+      const int mt = blk / NBN, nt0 = (blk % NBN) * BN;
+      f32x4 acc[BN];
+#pragma unroll
+      for (int j = 0; j < BN; ++j) acc[j] = zero4();
+      int kb = 0, ke = KMAX;
+      krange(mt, nt0, kb, ke);
+      for (int kk = kb; kk < ke; kk += M::KS) {
+        const typename M::frag a = frag_ld<T>(A, lda, 16 * mt, kk, lane, KMAX, arows);
+#pragma unroll
+        for (int j = 0; j < BN; ++j) {
+          const typename M::frag b = frag_ld<T>(Bt, ldb, 16 * (nt0 + j), kk, lane, KMAX, 1 << 30);
+          acc[j] = M::mma(a, b, acc[j]);
+        }
+      }
+      epi(it, mt, nt0, acc);
+    }
+  }
+}
+
+// D = A1 * B1 + A2 * B2 with one accumulator per tile (two contractions of different
+// lengths feeding the same output).
+template <class T, int MT, int NT, int BN, int NW, int KMAX1, int KMAX2, class KR1, class KR2, class EPI>
+__device__ __forceinline__ void block_gemm2(const T* A1, int lda1, const T* Bt1, int ldb1, KR1 kr1, const T* A2,
+                                            int lda2, const T* Bt2, int ldb2, KR2 kr2, EPI epi, int wave, int lane) {
+  typedef Mma<T> M;
+  constexpr int NBN = NT / BN;
+  constexpr int NB = MT * NBN;
+  constexpr int NIT = (NB + NW - 1) / NW;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int blk = wave + it * NW;
+    if (blk < NB) {
+      const int mt = blk / NBN, nt0 = (blk % NBN) * BN;
+      f32x4 acc[BN];
+#pragma unroll
+      for (int j = 0; j < BN; ++j) acc[j] = zero4();
+      int kb = 0, ke = KMAX1;
+      kr1(mt, nt0, kb, ke);
+      for (int kk = kb; kk < ke; kk += M::KS) {
+        const typename M::frag a = frag_ld<T>(A1, lda1, 16 * mt, kk, lane, KMAX1, 1 << 30);
+#pragma unroll
+        for (int j = 0; j < BN; ++j)
+          acc[j] = M::mma(a, frag_ld<T>(Bt1, ldb1, 16 * (nt0 + j), kk, lane, KMAX1, 1 << 30), acc[j]);
+      }
+      kb = 0;
+      ke = KMAX2;
+      kr2(mt, nt0, kb, ke);
+      for (int kk = kb; kk < ke; kk += M::KS) {
+        const typename M::frag a = frag_ld<T>(A2, lda2, 16 * mt, kk, lane, KMAX2, 1 << 30);
+#pragma unroll
+        for (int j = 0; j < BN; ++j)
+          acc[j] = M::mma(a, frag_ld<T>(Bt2, ldb2, 16 * (nt0 + j), kk, lane, KMAX2, 1 << 30), acc[j]);
+      }
+      epi(it, mt, nt0, acc);
+    }
+  }
+}
+
+// Contraction-range helpers for triangular operands (K step = KS, tiles of 16 rows).
+template <class T>
+__device__ __forceinline__ int round_dn(int x) { return (x / Mma<T>::KS) * Mma<T>::KS; }
+template <class T>
+__device__ __forceinline__ int round_up(int x) { return ((x + Mma<T>::KS - 1) / Mma<T>::KS) * Mma<T>::KS; }
+
+// Returns x unchanged but opaque to the optimiser, so values derived from it are
+// recomputed where they are used instead of being hoisted out of an enclosing loop and
+// kept live across it.
+__device__ __forceinline__ int opaque_v(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ int opaque_s(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+struct FullRange {
+  __device__ void operator()(int, int, int&, int&) const {}
+};
+
+}  // namespace kda

@@ -1,0 +1,55 @@
+// Host-side launchers of the KDA kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Problem geometry shared by every kernel.
+struct Shape {
+  int T;                 // tokens per sequence (dense) or total tokens (packed)
+  int H, HV;             // q/k heads, value heads
+  int N;                 // sequences
+  int NT;                // total chunks
+  float scale;
+  const int32_t* cu;     // device cu_seqlens, or nullptr when dense
+  const int32_t* choff;  // device first-chunk table [N+1], or nullptr when dense
+};
+
+// Per-chunk workspace tensors of the forward (all [NT, HV, ...]).
+struct FwdWs {
+  void* negw;  // [C][K]   -w, w = INV diag(beta) (k e^G)
+  void* krT;   // [K][C]   (k e^(gam-G))^T
+  void* uT;    // [V][C]   u^T, u = INV diag(beta) v
+  float* eg;   // [K]      e^gam
+};
+
+// Per-chunk workspace tensors of the backward (all [NT, HV, ...]).
+struct BwdWs {
+  void* kr;    // [C][K]   k e^(gam-G)
+  void* nwT;   // [K][C]   -w^T
+  void* bcT;   // [V][K]   (qd - Mqk w)^T dO, transposed
+  float* eg;   // [K]      e^gam
+  void* dS;    // [K][V]   gradient w.r.t. each chunk's S_out
+  void* yT;    // [V][C]   (kr dS)^T
+};
+
+// dtype: 0 = fp32 (K = V = C = 16), 1 = bf16 (K = V = 128, C in {16, 64}).
+hipError_t launch_chunk_offsets(const int32_t* cu, int N, int C, int32_t* choff, hipStream_t st);
+hipError_t launch_fwd_prep(int dtype, int C, const Shape& s, const void* k, const void* v, const float* g,
+                           const float* beta, void* inv, const FwdWs& ws, hipStream_t st);
+hipError_t launch_fwd_out(int dtype, int C, const Shape& s, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, const void* states, const void* inv, void* o,
+                          hipStream_t st);
+hipError_t launch_scan_fwd(int dtype, int C, const Shape& s, const FwdWs& ws, const void* h0, void* states,
+                           float* final_state, hipStream_t st);
+hipError_t launch_bwd_prep(int dtype, int C, const Shape& s, const void* q, const void* k, const float* g,
+                           const float* beta, const void* inv, const void* dO, const BwdWs& ws, hipStream_t st);
+hipError_t launch_scan_bwd(int dtype, int C, const Shape& s, const BwdWs& ws, const void* dSf, float* dh0,
+                           hipStream_t st);
+hipError_t launch_bwd_grad(int dtype, int C, const Shape& s, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const void* states, const void* inv, const void* dO,
+                           const BwdWs& ws, void* dq, void* dk, void* dv, float* dg, float* dbeta, hipStream_t st);
+
+}  // namespace kda

@@ -1,0 +1,188 @@
+// Sequential chunk scans of KDA for gfx950.
+//
+// Both directions are one affine step per chunk on a K x V fp32 matrix X:
+//   Y    = Z + P1 X                 (C x V, contraction over K)
+//   X'   = diag(e^gam) X + W + P2 Y (K x V, contraction over C)
+// Forward (FLA chunk_gated_delta_rule_fwd_h; FlashKDA page, the state update
+// S_new = S*exp(gT) + kr^T@U): X = S, P1 = -w, Z = u, P2 = kr^T, W = 0, so Y = U and
+// X' = S_out. Backward (FLA chunk_gated_delta_rule_bwd_dhu; FlashKDA page steps 2-3):
+// X = dS (gradient w.r.t. S_out), P1 = kr, Z = 0 so Y = kr dS, P2 = -w^T and
+// W = (qd - Mqk w)^T dO, giving X' = dS_in = diag(e^gam) dS + qd^T dO - w^T (Mqk^T dO + kr dS).
+//
+// The columns of X evolve independently, so one wavefront owns a 16-column slice of one
+// (sequence, head) and walks its chunks in order, keeping X in fp32 registers as MFMA
+// accumulator tiles. The accumulator tiles of X and Y are fed back as B operands with
+// the contraction index permuted (rows 16t + 4*grp + i of tile t map to lane group grp,
+// slot i), and the A operands are loaded in the same permuted order, so neither X nor Y
+// round-trips through LDS.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <class T, int K, int V, int C, bool FWD>
+__global__ __launch_bounds__(64) void scan_kernel(Shape s, const T* __restrict__ P1, const T* __restrict__ P2,
+                                                   const T* __restrict__ Zi, const T* __restrict__ Wi,
+                                                   const float* __restrict__ eg, const T* __restrict__ X0,
+                                                   T* __restrict__ Xout, T* __restrict__ Yout,
+                                                   float* __restrict__ Xfin) {
+  typedef Mma<T> M;
+  constexpr int KT = K / 16, CT = C / 16;
+  const int vt = blockIdx.x, h = blockIdx.y, nseq = blockIdx.z;
+  const int lane = threadIdx.x, n = lane & 15, grp = lane >> 4;
+  const int vcol = 16 * vt + n;
+  int c0, nc;
+  seq_range(nseq, s.cu, s.choff, s.T, C, c0, nc);
+  if (c0 + nc > s.NT) nc = max(0, s.NT - c0);
+
+  f32x4 X[KT];
+  if (X0 != nullptr) {
+    const T* x0 = X0 + ((long)nseq * s.HV + h) * K * V;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) X[t][j] = to_f(x0[(16 * t + 4 * grp + j) * V + vcol]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < KT; ++t) X[t] = zero4();
+  }
+
+  for (int ii = 0; ii < nc; ++ii) {
+    const int c = FWD ? c0 + ii : c0 + nc - 1 - ii;
+    const long ch = (long)c * s.HV + h;
+    // X entering this step: S_in (forward) or the gradient w.r.t. S_out (backward).
+    T* xo = Xout + ch * K * V;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xo[(16 * t + 4 * grp + j) * V + vcol] = from_f<T>(X[t][j]);
+
+    // Y = Z + P1 X
+    f32x4 Y[CT];
+    if (Zi != nullptr) {
+#pragma unroll
+      for (int m = 0; m < CT; ++m) Y[m] = ld4f(Zi + ch * V * C + vcol * C + 16 * m + 4 * grp);
+    } else {
+#pragma unroll
+      for (int m = 0; m < CT; ++m) Y[m] = zero4();
+    }
+    const T* p1 = P1 + ch * C * K;
+    if constexpr (M::PER == 8) {
+      static_assert(KT % 2 == 0, "bf16 scan pairs row tiles of X");
+#pragma unroll
+      for (int p = 0; p < KT / 2; ++p) {
+        bf16x8 b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b[i] = (bf16)X[2 * p][i];
+          b[4 + i] = (bf16)X[2 * p + 1][i];
+        }
+#pragma unroll
+        for (int m = 0; m < CT; ++m) {
+          const T* row = p1 + (16 * m + n) * K + 32 * p + 4 * grp;
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16);
+          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          Y[m] = M::mma(a, b, Y[m]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int m = 0; m < CT; ++m)
+            Y[m] = M::mma(to_f(p1[(16 * m + n) * K + 16 * t + 4 * grp + j]), X[t][j], Y[m]);
+    }
+    if (Yout != nullptr) {
+#pragma unroll
+      for (int m = 0; m < CT; ++m) st4(Yout + ch * V * C + vcol * C + 16 * m + 4 * grp, Y[m]);
+    }
+
+    // X' = W + P2 Y, then X = diag(e^gam) X + X'
+    f32x4 Xn[KT];
+    if (Wi != nullptr) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) Xn[t] = ld4f(Wi + ch * V * K + vcol * K + 16 * t + 4 * grp);
+    } else {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) Xn[t] = zero4();
+    }
+    const T* p2 = P2 + ch * K * C;
+    if constexpr (M::PER == 8) {
+#pragma unroll
+      for (int q = 0; q < (CT + 1) / 2; ++q) {
+        bf16x8 b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b[i] = (bf16)Y[2 * q][i];
+          b[4 + i] = 2 * q + 1 < CT ? (bf16)Y[2 * q + 1 < CT ? 2 * q + 1 : 0][i] : (bf16)0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          const T* row = p2 + (16 * t + n) * C + 32 * q + 4 * grp;
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
+          bf16x4 hi = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+          if (2 * q + 1 < CT) hi = *reinterpret_cast<const bf16x4*>(row + 16);
+          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          Xn[t] = M::mma(a, b, Xn[t]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < CT; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int t = 0; t < KT; ++t)
+            Xn[t] = M::mma(to_f(p2[(16 * t + n) * C + 16 * m + 4 * grp + j]), Y[m][j], Xn[t]);
+    }
+    const float* e = eg + ch * K;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) X[t] = ld4f(e + 16 * t + 4 * grp) * X[t] + Xn[t];
+  }
+
+  if (Xfin != nullptr) {
+    float* xf = Xfin + ((long)nseq * s.HV + h) * K * V;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xf[(16 * t + 4 * grp + j) * V + vcol] = X[t][j];
+  }
+}
+
+template <class T, int K, int V, int C, bool FWD>
+static hipError_t scan_t(const Shape& s, const void* P1, const void* P2, const void* Zi, const void* Wi,
+                         const float* eg, const void* X0, void* Xout, void* Yout, float* Xfin, hipStream_t st) {
+  if (s.N == 0) return hipSuccess;
+  hipLaunchKernelGGL((scan_kernel<T, K, V, C, FWD>), dim3(V / 16, s.HV, s.N), dim3(64), 0, st, s,
+                     static_cast<const T*>(P1), static_cast<const T*>(P2), static_cast<const T*>(Zi),
+                     static_cast<const T*>(Wi), eg, static_cast<const T*>(X0), static_cast<T*>(Xout),
+                     static_cast<T*>(Yout), Xfin);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_fwd(int dtype, int C, const Shape& s, const FwdWs& ws, const void* h0, void* states,
+                           float* final_state, hipStream_t st) {
+  if (dtype == 0)
+    return scan_t<float, 16, 16, 16, true>(s, ws.negw, ws.krT, ws.uT, nullptr, ws.eg, h0, states, nullptr,
+                                           final_state, st);
+  if (C == 64)
+    return scan_t<bf16, 128, 128, 64, true>(s, ws.negw, ws.krT, ws.uT, nullptr, ws.eg, h0, states, nullptr,
+                                            final_state, st);
+  return scan_t<bf16, 128, 128, 16, true>(s, ws.negw, ws.krT, ws.uT, nullptr, ws.eg, h0, states, nullptr,
+                                          final_state, st);
+}
+
+hipError_t launch_scan_bwd(int dtype, int C, const Shape& s, const BwdWs& ws, const void* dSf, float* dh0,
+                           hipStream_t st) {
+  if (dtype == 0)
+    return scan_t<float, 16, 16, 16, false>(s, ws.kr, ws.nwT, nullptr, ws.bcT, ws.eg, dSf, ws.dS, ws.yT, dh0, st);
+  if (C == 64)
+    return scan_t<bf16, 128, 128, 64, false>(s, ws.kr, ws.nwT, nullptr, ws.bcT, ws.eg, dSf, ws.dS, ws.yT, dh0,
+                                             st);
+  return scan_t<bf16, 128, 128, 16, false>(s, ws.kr, ws.nwT, nullptr, ws.bcT, ws.eg, dSf, ws.dS, ws.yT, dh0, st);
+}
+
+}  // namespace kda
