@@ -122,8 +122,10 @@ def main():
     def new_events(n):
         arr = (ctypes.c_void_p * n)()
         for i in range(n):
-            if hip.hipEventCreate(ctypes.byref(arr, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+            ev = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev.value
         return arr
 
     def elapsed(e0, e1):

@@ -292,15 +292,15 @@ __global__ __launch_bounds__(256) void fwd_out_kernel(Shape s, const T* __restri
 #pragma unroll
                                      for (int jb = 0; jb < BN; ++jb) {
                                        const int col = 16 * (nt0 + jb) + n;
-                                       f32x4 vc;
+                                       f32x4 vc4;
 #pragma unroll
                                        for (int j = 0; j < 4; ++j) {
                                          const int row = 16 * mt + 4 * grp + j;
                                          const float vv =
                                              row < len ? to_f(vc[row * vs + col]) : 0.f;
-                                         vc[j] = betas[row] * (vv - acc[jb][j]);
+                                         vc4[j] = betas[row] * (vv - acc[jb][j]);
                                        }
-                                       st4(VcT + col * LDC + 16 * mt + 4 * grp, vc);
+                                       st4(VcT + col * LDC + 16 * mt + 4 * grp, vc4);
                                      }
                                    }, wave, lane);
   // Mqk = tril(qd ki^T), row-major.
