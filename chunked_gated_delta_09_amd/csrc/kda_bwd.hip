@@ -25,6 +25,7 @@ namespace kda {
 
 template <class T, int K, int V, int C>
 struct BwdPrepLds {
+  static constexpr int NW = 8;
   static constexpr int P = pad_of<T>();
   static constexpr int LDK = K + P, LDC = C + P;
   static constexpr size_t oQd = 0;
@@ -41,12 +42,13 @@ struct BwdPrepLds {
 
 // One workgroup per (chunk, value head).
 template <class T, int K, int V, int C>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
+__global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
                                                         const float* __restrict__ gp, const float* __restrict__ bp,
                                                         const T* __restrict__ invp, const T* __restrict__ dOp,
                                                         BwdWs ws) {
   typedef BwdPrepLds<T, K, V, C> Lay;
-  constexpr int NW = 4, RT = C / 16, KT = K / 16, VT = V / 16;
+  constexpr int NW = Lay::NW, NTH = 64 * NW, RT = C / 16, KT = K / 16, VT = V / 16;
+  constexpr int NCK = (KT + NW - 1) / NW, NCV = (VT + NW - 1) / NW, NI = (C * C + NTH - 1) / NTH;
   constexpr int LDK = Lay::LDK, LDC = Lay::LDC;
   __shared__ __align__(16) unsigned char smem[Lay::total];
   T* Qd = reinterpret_cast<T*>(smem + Lay::oQd);
@@ -67,64 +69,82 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Shape s, const T* __restr
   const int len = geo.len;
   if (len <= 0) return;
   const int qs = s.H * K, gs = s.HV * K, vs = s.HV * V;
-  const T* qc = qp + (geo.bos * s.H + hq) * K;
-  const T* kc = kp + (geo.bos * s.H + hq) * K;
-  const float* gc = gp + (geo.bos * s.HV + h) * K;
-  const T* dOc = dOp + (geo.bos * s.HV + h) * V;
-  const float* bc = bp + geo.bos * s.HV + h;
+  const T* __restrict__ qc = qp + (geo.bos * s.H + hq) * K;
+  const T* __restrict__ kc = kp + (geo.bos * s.H + hq) * K;
+  const float* __restrict__ gc = gp + (geo.bos * s.HV + h) * K;
+  const T* __restrict__ dOc = dOp + (geo.bos * s.HV + h) * V;
+  const float* __restrict__ bc = bp + geo.bos * s.HV + h;
+  const T* __restrict__ invc = invp + ch * C * C;
+  T* __restrict__ krg = reinterpret_cast<T*>(ws.kr) + ch * C * K;
+  float* __restrict__ egc = ws.eg + ch * K;
 
-  if (tid < C) betas[tid] = tid < len ? bc[tid * s.HV] : 0.f;
+  // ---- every global load of the chunk, issued before any use
+  if (tid < C) betas[tid] = tid < len ? bc[min(tid, len - 1) * s.HV] : 0.f;
+  float G[NCK][RT][4], qv[NCK][RT][4], kv[NCK][RT][4], dov[NCV][RT][4];
+#pragma unroll
+  for (int ci = 0; ci < NCK; ++ci) {
+    const int kt = wave + ci * NW;
+    if (kt < KT) {
+      col_load<float, RT>(G[ci], gc, gs, 16 * kt + n, grp, len);
+      col_load<T, RT>(qv[ci], qc, qs, 16 * kt + n, grp, len);
+      col_load<T, RT>(kv[ci], kc, qs, 16 * kt + n, grp, len);
+    }
+  }
+#pragma unroll
+  for (int cv = 0; cv < NCV; ++cv) {
+    const int vt = wave + cv * NW;
+    if (vt < VT) col_load<T, RT>(dov[cv], dOc, vs, 16 * vt + n, grp, len);
+  }
+  T invr[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = tid + i * NTH;
+    invr[i] = idx < C * C ? invc[idx] : (T)0.0f;
+  }
   __syncthreads();
 
-  T* krg = reinterpret_cast<T*>(ws.kr) + ch * C * K;
-  for (int kt = wave; kt < KT; kt += NW) {
-    const int col = 16 * kt + n;
-    float G[RT][4];
+  // ---- gate cumsum and the decayed keys / queries
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+  for (int ci = 0; ci < NCK; ++ci) {
+    const int kt = wave + ci * NW;
+    if (kt < KT) {
+      const int col = 16 * kt + n;
+      col_prefix<RT>(G[ci], lane);
+      const float gam = __shfl(G[ci][RT - 1][3], n + 48, 64);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rt + 4 * grp + j;
-        G[rt][j] = row < len ? gc[row * gs + col] : 0.f;
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 bk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * rt + 4 * grp + j;
+          const float e = __expf(G[ci][rt][j]);
+          Qd[row * LDK + col] = from_f<T>(s.scale * qv[ci][rt][j] * e);
+          Ki[row * LDK + col] = from_f<T>(kv[ci][rt][j] * __expf(-G[ci][rt][j]));
+          bk[j] = betas[row] * kv[ci][rt][j] * e;
+          krg[row * K + col] = from_f<T>(kv[ci][rt][j] * __expf(gam - G[ci][rt][j]));
+        }
+        st4(BKdT + col * LDC + 16 * rt + 4 * grp, bk);
       }
-    col_prefix<RT>(G, lane);
-    const float gam = __shfl(G[RT - 1][3], n + 48, 64);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 bk;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rt + 4 * grp + j;
-        const int off = row * qs + col;
-        const float kv = row < len ? to_f(kc[off]) : 0.f;
-        const float qv = row < len ? to_f(qc[off]) : 0.f;
-        const float e = __expf(G[rt][j]);
-        Qd[row * LDK + col] = from_f<T>(s.scale * qv * e);
-        Ki[row * LDK + col] = from_f<T>(kv * __expf(-G[rt][j]));
-        bk[j] = betas[row] * kv * e;
-        krg[row * K + col] = from_f<T>(kv * __expf(gam - G[rt][j]));
-      }
-      st4(BKdT + col * LDC + 16 * rt + 4 * grp, bk);
-    }
-    if (grp == 0) ws.eg[ch * K + col] = __expf(gam);
-  }
-  for (int vt = wave; vt < VT; vt += NW) {
-    const int col = 16 * vt + n;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 d4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rt + 4 * grp + j;
-        d4[j] = row < len ? to_f(dOc[row * vs + col]) : 0.f;
-      }
-      st4(DoT + col * LDC + 16 * rt + 4 * grp, d4);
+      if (grp == 0) egc[col] = __expf(gam);
     }
   }
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int i = idx / C, j = idx % C;
-    const float val = (i < len && j < len) ? to_f(invp[ch * C * C + idx]) : (i == j ? 1.f : 0.f);
-    INVt[i * LDC + j] = from_f<T>(val);
+#pragma unroll
+  for (int cv = 0; cv < NCV; ++cv) {
+    const int vt = wave + cv * NW;
+    if (vt < VT) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        st4(DoT + (16 * vt + n) * LDC + 16 * rt + 4 * grp,
+            f32x4{dov[cv][rt][0], dov[cv][rt][1], dov[cv][rt][2], dov[cv][rt][3]});
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = tid + i * NTH;
+    if (idx < C * C) {
+      const int r = idx / C, cc = idx % C;
+      INVt[r * LDC + cc] = (r < len && cc < len) ? invr[i] : from_f<T>(r == cc ? 1.f : 0.f);
+    }
   }
   __syncthreads();
 
@@ -616,7 +636,7 @@ template <class T, int K, int V, int C>
 static hipError_t bwd_prep_t(const Shape& s, const void* q, const void* k, const float* g, const float* beta,
                              const void* inv, const void* dO, const BwdWs& ws, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C>), dim3(s.NT, s.HV), dim3(256), 0, st, s,
+  hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C>), dim3(s.NT, s.HV), dim3(64 * BwdPrepLds<T, K, V, C>::NW), 0, st, s,
                      static_cast<const T*>(q), static_cast<const T*>(k), g, beta, static_cast<const T*>(inv),
                      static_cast<const T*>(dO), ws);
   return hipGetLastError();

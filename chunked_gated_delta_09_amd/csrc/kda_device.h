@@ -69,13 +69,17 @@ constexpr int pad_of() { return 16 / (int)sizeof(T); }
 // >= kmax and rows >= rmax read as zero (kmax must be a multiple of PER).
 // Offsets are 32-bit: bases are per-chunk (wave-uniform) pointers and a chunk spans far
 // fewer than 2^31 elements.
+// The load itself is unconditional (from a clamped, valid row and column) and the zero is
+// selected afterwards, so masked loads do not turn into branches that serialise them.
 template <class T>
 __device__ __forceinline__ typename Mma<T>::frag frag_ld(const T* base, int ld, int r0, int k0, int lane,
                                                            int kmax, int rmax) {
   const int r = r0 + (lane & 15);
   const int kk = k0 + Mma<T>::PER * (lane >> 4);
-  if (kk >= kmax || r >= rmax) return Mma<T>::zero();
-  return *reinterpret_cast<const typename Mma<T>::frag*>(base + (r * ld + kk));
+  const bool ok = kk < kmax && r < rmax;
+  const typename Mma<T>::frag v =
+      *reinterpret_cast<const typename Mma<T>::frag*>(base + ((ok ? r : 0) * ld + (ok ? kk : 0)));
+  return ok ? v : Mma<T>::zero();
 }
 
 // Same without bounds (all indices known to be valid).
@@ -161,6 +165,26 @@ __device__ __forceinline__ void seq_range(int n, const int32_t* cu, const int32_
 // 4-element in-lane scan plus an exchange of block totals among the 4 lanes
 // (l%16, l%16 + 16, +32, +48) that share a column.
 // ---------------------------------------------------------------------------------
+
+// Loads rows 16*rt + 4*grp + j (rt < RT, j < 4) of column `col` of a row-major chunk tile
+// (row stride ld elements; rows >= len read as zero; needs len >= 1). Every load is issued
+// unconditionally before any value is used, so a wave has all of them in flight at once.
+template <class T, int RT>
+__device__ __forceinline__ void col_load(float (&x)[RT][4], const T* __restrict__ base, int ld, int col, int grp,
+                                         int len) {
+  T raw[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * rt + 4 * grp + j;
+      raw[rt][j] = base[min(row, len - 1) * ld + col];  // len >= 1: always a valid row
+    }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[rt][j] = 16 * rt + 4 * grp + j < len ? to_f(raw[rt][j]) : 0.f;
+}
 
 // Inclusive prefix sum over rows of one column: x[rt][j] holds row 16*rt + 4*grp + j.
 template <int RT>
