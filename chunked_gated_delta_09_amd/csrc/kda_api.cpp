@@ -106,13 +106,20 @@ struct BwdLayout {
   size_t choff, kr, nwT, bcT, eg, dS, yT, total;
 };
 
+// Elements per chunk-head of the scan's K x C operand: the bf16 path stores it in
+// fragment order, padded to whole 32-wide contraction steps.
+size_t p2_elems(const Plan& p) {
+  if (p.dtype == KDA_BF16) return (size_t)(p.K / 16) * ((p.C / 16 + 1) / 2) * 64 * 8;
+  return (size_t)p.K * p.C;
+}
+
 FwdLayout fwd_layout(const kda_dims* d, const Plan& p) {
   FwdLayout L;
   const size_t nth = (size_t)p.NT * d->HV;
   size_t o = 0;
   L.choff = o; o = align_up(o + sizeof(int32_t) * (d->N + 1));
   L.negw = o; o = align_up(o + nth * p.C * p.K * p.es);
-  L.krT = o; o = align_up(o + nth * p.K * p.C * p.es);
+  L.krT = o; o = align_up(o + nth * p2_elems(p) * p.es);
   L.uT = o; o = align_up(o + nth * p.V * p.C * p.es);
   L.eg = o; o = align_up(o + nth * p.K * sizeof(float));
   L.total = o;
@@ -125,7 +132,7 @@ BwdLayout bwd_layout(const kda_dims* d, const Plan& p) {
   size_t o = 0;
   L.choff = o; o = align_up(o + sizeof(int32_t) * (d->N + 1));
   L.kr = o; o = align_up(o + nth * p.C * p.K * p.es);
-  L.nwT = o; o = align_up(o + nth * p.K * p.C * p.es);
+  L.nwT = o; o = align_up(o + nth * p2_elems(p) * p.es);
   L.bcT = o; o = align_up(o + nth * p.V * p.K * p.es);
   L.eg = o; o = align_up(o + nth * p.K * sizeof(float));
   L.dS = o; o = align_up(o + nth * p.K * p.V * p.es);

@@ -121,7 +121,12 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
           Qd[row * LDK + col] = from_f<T>(s.scale * qv[ci][rt][j] * e);
           Ki[row * LDK + col] = from_f<T>(kv[ci][rt][j] * __expf(-G[ci][rt][j]));
           bk[j] = betas[row] * kv[ci][rt][j] * e;
-          krg[row * K + col] = from_f<T>(kv[ci][rt][j] * __expf(gam - G[ci][rt][j]));
+          const T krv = from_f<T>(kv[ci][rt][j] * __expf(gam - G[ci][rt][j]));
+          if constexpr (sizeof(T) == 2) {
+            krg[ScanFrag<K, V, C>::p1(row, col)] = krv;
+          } else {
+            krg[row * K + col] = krv;
+          }
         }
         st4(BKdT + col * LDC + 16 * rt + 4 * grp, bk);
       }
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
         }
       }, wave, lane);
   // w = INV diag(beta) kd: kept transposed in LDS, stored negated and transposed for the scan.
-  T* nwT = reinterpret_cast<T*>(ws.nwT) + ch * K * C;
+  T* __restrict__ nwT = reinterpret_cast<T*>(ws.nwT) + ch * (sizeof(T) == 2 ? ScanFrag<K, V, C>::P2_ELEMS : K * C);
   constexpr int BNK = KT % 2 == 0 ? 2 : 1;
   block_gemm<T, RT, KT, BNK, NW, C>(
       INVt, LDC, 1 << 30, BKdT, LDC, [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
@@ -168,7 +173,11 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
         for (int jb = 0; jb < BNK; ++jb) {
           const int col = 16 * (nt0 + jb) + n;
           st4(WT + col * LDC + 16 * mt + 4 * grp, acc[jb]);
-          st4(nwT + col * C + 16 * mt + 4 * grp, -acc[jb]);
+          if constexpr (sizeof(T) == 2) {
+            st4(nwT + ScanFrag<K, V, C>::p2(col, 16 * mt + 4 * grp), -acc[jb]);
+          } else {
+            st4(nwT + col * C + 16 * mt + 4 * grp, -acc[jb]);
+          }
         }
       }, wave, lane);
   __syncthreads();
@@ -187,13 +196,17 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
       }, wave, lane);
   __syncthreads();
   // W = Q'^T dO, stored transposed [V][K].
-  T* bcT = reinterpret_cast<T*>(ws.bcT) + ch * V * K;
+  T* __restrict__ bcT = reinterpret_cast<T*>(ws.bcT) + ch * V * K;
   constexpr int BNV = VT % 2 == 0 ? 2 : 1;
   block_gemm<T, KT, VT, BNV, NW, C>(QpT, LDC, 1 << 30, DoT, LDC, FullRange(),
                                     [&](int, int mt, int nt0, f32x4(&acc)[BNV]) {
 #pragma unroll
                                       for (int jb = 0; jb < BNV; ++jb)
-                                        st4(bcT + (16 * (nt0 + jb) + n) * K + 16 * mt + 4 * grp, acc[jb]);
+                                        if constexpr (sizeof(T) == 2) {
+                                          st4(bcT + ScanFrag<K, V, C>::seed(nt0 + jb, mt, KT, lane), acc[jb]);
+                                        } else {
+                                          st4(bcT + (16 * (nt0 + jb) + n) * K + 16 * mt + 4 * grp, acc[jb]);
+                                        }
                                     }, wave, lane);
 }
 

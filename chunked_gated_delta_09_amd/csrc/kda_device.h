@@ -337,6 +337,38 @@ __device__ __forceinline__ void block_gemm2(const T* A1, int lda1, const T* Bt1,
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Fragment order of the chunk-scan operands (bf16 path). Per chunk and head:
+//   P1 (C x K, the A operand of Y = Z + P1 X):   [C/16][K/32][64 lanes][8]
+//   P2 (K x C, the A operand of X' = W + P2 Y):  [K/16][ceil(C/32)][64 lanes][8]
+//   Z  (C x V) and W (K x V) accumulator seeds:  [V/16][rows/16][64 lanes][4]
+// Lane l = n + 16*g of A fragment (row tile m, contraction pair p) holds row 16m + n at
+// contraction indices 32p + 4g + i (slots 0-3) and 32p + 16 + 4g + i (slots 4-7): the
+// order in which the scan feeds two accumulator tiles of X (or Y) as one B operand. A
+// wave loads one fragment as one contiguous 1 KB block, and the accumulator seeds are
+// stored exactly as an accumulator tile is laid out across the lanes.
+// ---------------------------------------------------------------------------------
+template <int K, int V, int C>
+struct ScanFrag {
+  static constexpr int KT = K / 16, CT = C / 16, VT = V / 16, KP = K / 32, CQ = (CT + 1) / 2;
+  static constexpr int P1_ELEMS = CT * KP * 64 * 8;
+  static constexpr int P2_ELEMS = KT * CQ * 64 * 8;
+  // element offset of P1[r][k]
+  __device__ __forceinline__ static int p1(int r, int k) {
+    const int kk = k & 31;
+    return (((r >> 4) * KP + (k >> 5)) * 64 + (r & 15) + 16 * ((kk & 15) >> 2)) * 8 + 4 * (kk >> 4) + (kk & 3);
+  }
+  // element offset of P2[r][c]
+  __device__ __forceinline__ static int p2(int r, int c) {
+    const int cc = c & 31;
+    return (((r >> 4) * CQ + (c >> 5)) * 64 + (r & 15) + 16 * ((cc & 15) >> 2)) * 8 + 4 * (cc >> 4) + (cc & 3);
+  }
+  // element offset of the 4 values lane `lane` holds of seed tile (column tile vt, row tile m)
+  __device__ __forceinline__ static int seed(int vt, int m, int rows16, int lane) {
+    return ((vt * rows16 + m) * 64 + lane) * 4;
+  }
+};
+
 // Contraction-range helpers for triangular operands (K step = KS, tiles of 16 rows).
 template <class T>
 __device__ __forceinline__ int round_dn(int x) { return (x / Mma<T>::KS) * Mma<T>::KS; }

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(Shape s, const T* __restr
       }
     col_prefix<RT>(G, lane);
     const float gam = __shfl(G[RT - 1][3], n + 48, 64);
-    T* krT = reinterpret_cast<T*>(ws.krT) + ch * K * C;
+    T* __restrict__ krT = reinterpret_cast<T*>(ws.krT) + ch * (sizeof(T) == 2 ? ScanFrag<K, V, C>::P2_ELEMS : K * C);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 bk, kr4;
@@ -116,7 +116,11 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(Shape s, const T* __restr
         kr4[j] = kv * __expf(gam - G[rt][j]);
       }
       st4(BKdT + col * LDC + 16 * rt + 4 * grp, bk);
-      st4(krT + col * C + 16 * rt + 4 * grp, kr4);
+      if constexpr (sizeof(T) == 2) {
+        st4(krT + ScanFrag<K, V, C>::p2(col, 16 * rt + 4 * grp), kr4);
+      } else {
+        st4(krT + col * C + 16 * rt + 4 * grp, kr4);
+      }
     }
     if (grp == 0) ws.eg[ch * K + col] = __expf(gam);
   }
@@ -174,7 +178,11 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(Shape s, const T* __restr
       BKdT, LDC, 1 << 30, INVt, LDC,
       [](int, int nt0, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (nt0 + 1))); },
       [&](int, int mt, int nt0, f32x4(&acc)[1]) {
-        st4(negw + (16 * nt0 + n) * K + 16 * mt + 4 * grp, -acc[0]);
+        if constexpr (sizeof(T) == 2) {
+          st4(negw + ScanFrag<K, V, C>::p1(16 * nt0 + n, 16 * mt + 4 * grp), -acc[0]);
+        } else {
+          st4(negw + (16 * nt0 + n) * K + 16 * mt + 4 * grp, -acc[0]);
+        }
       }, wave, lane);
   // u = INV diag(beta) v, stored transposed [V][C].
   T* uT = reinterpret_cast<T*>(ws.uT) + ch * V * C;
@@ -185,7 +193,11 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(Shape s, const T* __restr
       [&](int, int mt, int nt0, f32x4(&acc)[BN]) {
 #pragma unroll
         for (int jb = 0; jb < BN; ++jb)
-          st4(uT + (16 * (nt0 + jb) + n) * C + 16 * mt + 4 * grp, acc[jb]);
+          if constexpr (sizeof(T) == 2) {
+            st4(uT + ScanFrag<K, V, C>::seed(nt0 + jb, mt, RT, lane), acc[jb]);
+          } else {
+            st4(uT + (16 * (nt0 + jb) + n) * C + 16 * mt + 4 * grp, acc[jb]);
+          }
       }, wave, lane);
 }
 

@@ -1,4 +1,5 @@
-// Sequential chunk scans of KDA for gfx950.
+// Sequential chunk scans of KDA for gfx950. The fp32 path (small K, V, C) reads its
+// operands in plain row-major order; the bf16 path reads them in fragment order.
 //
 // Both directions are one affine step per chunk on a K x V fp32 matrix X:
 //   Y    = Z + P1 X                 (C x V, contraction over K)
@@ -152,14 +153,172 @@ __global__ __launch_bounds__(64) void scan_kernel(Shape s, const T* __restrict__
   }
 }
 
+
+// bf16 path: the per-chunk operands are stored in fragment order (ScanFrag), so each wave
+// load is a contiguous 1 KB block, and the next chunk's operands are loaded into registers
+// while the current chunk is computed (the index is clamped, so the loads are
+// unconditional and always in flight).
+template <int K, int V, int C, bool FWD>
+__global__ __launch_bounds__(64) void scan_bf16_kernel(Shape s, const bf16* __restrict__ P1,
+                                                        const bf16* __restrict__ P2, const bf16* __restrict__ Zs,
+                                                        const bf16* __restrict__ Ws, const float* __restrict__ eg,
+                                                        const bf16* __restrict__ X0, bf16* __restrict__ Xout,
+                                                        bf16* __restrict__ Yout, float* __restrict__ Xfin) {
+  typedef ScanFrag<K, V, C> F;
+  typedef Mma<bf16> M;
+  constexpr int KT = F::KT, CT = F::CT, KP = F::KP, CQ = F::CQ;
+  static_assert(KT % 2 == 0, "the bf16 scan pairs row tiles of X");
+  const int vt = blockIdx.x, h = blockIdx.y, nseq = blockIdx.z;
+  const int lane = threadIdx.x, n = lane & 15, grp = lane >> 4;
+  const int vcol = 16 * vt + n;
+  int c0, nc;
+  seq_range(nseq, s.cu, s.choff, s.T, C, c0, nc);
+  if (c0 + nc > s.NT) nc = max(0, s.NT - c0);
+
+  struct Ops {
+    bf16x8 a1[CT][KP];
+    bf16x8 a2[KT][CQ];
+    bf16x4 w[KT];
+    bf16x4 z[CT];
+    f32x4 e[KT];
+  };
+  auto load = [&](int c, Ops& o) {
+    const long ch = (long)c * s.HV + h;
+    const bf16x8* p1 = reinterpret_cast<const bf16x8*>(P1 + ch * F::P1_ELEMS) + lane;
+#pragma unroll
+    for (int m = 0; m < CT; ++m)
+#pragma unroll
+      for (int p = 0; p < KP; ++p) o.a1[m][p] = p1[(m * KP + p) * 64];
+    const bf16x8* p2 = reinterpret_cast<const bf16x8*>(P2 + ch * F::P2_ELEMS) + lane;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int q = 0; q < CQ; ++q) o.a2[t][q] = p2[(t * CQ + q) * 64];
+    if constexpr (!FWD) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) o.w[t] = *reinterpret_cast<const bf16x4*>(Ws + ch * K * V + F::seed(vt, t, KT, lane));
+    }
+    if constexpr (FWD) {
+#pragma unroll
+      for (int m = 0; m < CT; ++m) o.z[m] = *reinterpret_cast<const bf16x4*>(Zs + ch * C * V + F::seed(vt, m, CT, lane));
+    }
+#pragma unroll
+    for (int t = 0; t < KT; ++t) o.e[t] = *reinterpret_cast<const f32x4*>(eg + ch * K + 16 * t + 4 * grp);
+  };
+
+  f32x4 X[KT];
+  if (X0 != nullptr) {
+    const bf16* x0 = X0 + ((long)nseq * s.HV + h) * K * V;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) X[t][j] = (float)x0[(16 * t + 4 * grp + j) * V + vcol];
+  } else {
+#pragma unroll
+    for (int t = 0; t < KT; ++t) X[t] = zero4();
+  }
+
+  if (nc > 0) {
+    Ops cur;
+    load(FWD ? c0 : c0 + nc - 1, cur);
+    for (int ii = 0; ii < nc; ++ii) {
+      const int c = FWD ? c0 + ii : c0 + nc - 1 - ii;
+      const int in = min(ii + 1, nc - 1);
+      Ops nxt;
+      load(FWD ? c0 + in : c0 + nc - 1 - in, nxt);
+      const long ch = (long)c * s.HV + h;
+
+      bf16* xo = Xout + ch * K * V;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xo[(16 * t + 4 * grp + j) * V + vcol] = (bf16)X[t][j];
+
+      // Y = Z + P1 X
+      f32x4 Y[CT];
+#pragma unroll
+      for (int m = 0; m < CT; ++m) {
+        if constexpr (FWD) {
+          Y[m] = f32x4{(float)cur.z[m][0], (float)cur.z[m][1], (float)cur.z[m][2], (float)cur.z[m][3]};
+        } else {
+          Y[m] = zero4();
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < KP; ++p) {
+        bf16x8 b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b[i] = (bf16)X[2 * p][i];
+          b[4 + i] = (bf16)X[2 * p + 1][i];
+        }
+#pragma unroll
+        for (int m = 0; m < CT; ++m) Y[m] = M::mma(cur.a1[m][p], b, Y[m]);
+      }
+      if (Yout != nullptr) {
+#pragma unroll
+        for (int m = 0; m < CT; ++m) st4(Yout + ch * V * C + vcol * C + 16 * m + 4 * grp, Y[m]);
+      }
+
+      // X' = W + P2 Y;  X = diag(e^gam) X + X'
+      f32x4 Xn[KT];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        if constexpr (!FWD) {
+          Xn[t] = f32x4{(float)cur.w[t][0], (float)cur.w[t][1], (float)cur.w[t][2], (float)cur.w[t][3]};
+        } else {
+          Xn[t] = zero4();
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < CQ; ++q) {
+        const bool pair = 2 * q + 1 < CT;
+        bf16x8 b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b[i] = (bf16)Y[2 * q][i];
+          b[4 + i] = pair ? (bf16)Y[pair ? 2 * q + 1 : 2 * q][i] : (bf16)0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          bf16x8 a = cur.a2[t][q];
+          if (!pair) {
+#pragma unroll
+            for (int i = 4; i < 8; ++i) a[i] = (bf16)0.0f;
+          }
+          Xn[t] = M::mma(a, b, Xn[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < KT; ++t) X[t] = cur.e[t] * X[t] + Xn[t];
+      cur = nxt;
+    }
+  }
+
+  if (Xfin != nullptr) {
+    float* xf = Xfin + ((long)nseq * s.HV + h) * K * V;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xf[(16 * t + 4 * grp + j) * V + vcol] = X[t][j];
+  }
+}
+
 template <class T, int K, int V, int C, bool FWD>
 static hipError_t scan_t(const Shape& s, const void* P1, const void* P2, const void* Zi, const void* Wi,
                          const float* eg, const void* X0, void* Xout, void* Yout, float* Xfin, hipStream_t st) {
   if (s.N == 0) return hipSuccess;
-  hipLaunchKernelGGL((scan_kernel<T, K, V, C, FWD>), dim3(V / 16, s.HV, s.N), dim3(64), 0, st, s,
-                     static_cast<const T*>(P1), static_cast<const T*>(P2), static_cast<const T*>(Zi),
-                     static_cast<const T*>(Wi), eg, static_cast<const T*>(X0), static_cast<T*>(Xout),
-                     static_cast<T*>(Yout), Xfin);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((scan_bf16_kernel<K, V, C, FWD>), dim3(V / 16, s.HV, s.N), dim3(64), 0, st, s,
+                       static_cast<const bf16*>(P1), static_cast<const bf16*>(P2), static_cast<const bf16*>(Zi),
+                       static_cast<const bf16*>(Wi), eg, static_cast<const bf16*>(X0), static_cast<bf16*>(Xout),
+                       static_cast<bf16*>(Yout), Xfin);
+  } else {
+    hipLaunchKernelGGL((scan_kernel<T, K, V, C, FWD>), dim3(V / 16, s.HV, s.N), dim3(64), 0, st, s,
+                       static_cast<const T*>(P1), static_cast<const T*>(P2), static_cast<const T*>(Zi),
+                       static_cast<const T*>(Wi), eg, static_cast<const T*>(X0), static_cast<T*>(Xout),
+                       static_cast<T*>(Yout), Xfin);
+  }
   return hipGetLastError();
 }
 
