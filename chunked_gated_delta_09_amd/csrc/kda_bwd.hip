@@ -239,7 +239,10 @@ struct GradLds {
 };
 
 // One workgroup per (chunk, q/k head); the value heads of the group are processed in
-// turn and their dq, dk contributions summed in registers.
+// turn and their dq, dk contributions summed in registers. Each phase issues all of its
+// global loads before using any of them; q, k and the gate cumsum G stay in registers
+// for the whole value head, and dO is read from HBM once (as 16-byte row vectors) and
+// staged in LDS transposed (for dU) and then row-major (for dMqk and dq).
 template <class T, int K, int V, int C>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
                                                         const T* __restrict__ vp, const float* __restrict__ gp,
@@ -250,11 +253,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
                                                         float* __restrict__ dbp) {
   typedef GradLds<T, K, V, C> Lay;
   typedef Mma<T> M;
-  constexpr int NW = Lay::NW, RT = C / 16, KT = K / 16, VT = V / 16;
-  constexpr int NCT = (KT + NW - 1) / NW;
+  typedef T vecT __attribute__((ext_vector_type(16 / sizeof(T))));
+  constexpr int NW = Lay::NW, NTH = 64 * NW, RT = C / 16, KT = K / 16, VT = V / 16;
+  constexpr int NCT = (KT + NW - 1) / NW, NCV = (VT + NW - 1) / NW, NI = (C * C + NTH - 1) / NTH;
+  constexpr int VEC = 16 / (int)sizeof(T), NVEC = C * V / VEC, NDV = (NVEC + NTH - 1) / NTH;
   constexpr int LDK = Lay::LDK, LDC = Lay::LDC, LDV = Lay::LDV;
   constexpr int BN1 = VT % 2 == 0 ? 2 : 1;
   constexpr int NIT1 = (RT * (VT / BN1) + NW - 1) / NW;
+  constexpr int NITC = (RT * RT + NW - 1) / NW;
+  constexpr int NKV = V / M::KS;
   __shared__ __align__(16) unsigned char smem[Lay::total];
   T* Qd = reinterpret_cast<T*>(smem + Lay::oQd);
   T* Kd = reinterpret_cast<T*>(smem + Lay::oKd);
@@ -276,18 +283,17 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
   T* MqkT = reinterpret_cast<T*>(smem + Lay::oMqkT);
   float* betas = reinterpret_cast<float*>(smem + Lay::oBeta);
   float* dbpart = reinterpret_cast<float*>(smem + Lay::oDbp);
-  T* DoT = reinterpret_cast<T*>(smem + Lay::oDoT);
+  T* DoT = reinterpret_cast<T*>(smem + Lay::oDoT);  // dO^T, then dO row-major (same slot)
+  T* DoR = DoT;
 
   const int c = blockIdx.x, hq = blockIdx.y;
   const int Gq = s.HV / s.H;
   const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, grp = lane >> 4;
-  const int len = geo.len;
+  if (geo.len <= 0) return;
   const long bos = geo.bos;
-  if (len <= 0) return;
   const int qs = s.H * K, gs = s.HV * K, vs = s.HV * V;
-  const T* qc = qp + (bos * s.H + hq) * K;
-  const T* kc = kp + (bos * s.H + hq) * K;
+  const T* __restrict__ qc = qp + (bos * s.H + hq) * K;
+  const T* __restrict__ kc = kp + (bos * s.H + hq) * K;
 
   float dqa[NCT][RT][4], dka[NCT][RT][4];
 #pragma unroll
@@ -299,41 +305,69 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 
   for (int e = 0; e < Gq; ++e) {
     const int h = hq * Gq + e;
+    const long ch = (long)c * s.HV + h;
     // Per-iteration opaque copies: keep lane-dependent addresses and row masks from being
     // hoisted out of this loop (which would hold hundreds of them live across its body).
     const int tid = opaque_v(threadIdx.x);
     const int lane = tid & 63, n = lane & 15, grp = lane >> 4;
     const int wave = opaque_s(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
     const int len = opaque_s(__builtin_amdgcn_readfirstlane(geo.len));
-    const long ch = (long)c * s.HV + h;
-    const T* Sin = states + ch * K * V;
-    const T* dSo = reinterpret_cast<const T*>(ws.dS) + ch * K * V;
-    const T* dOc = dOp + (bos * s.HV + h) * V;  // row stride HV*V
-    const T* vc = vp + (bos * s.HV + h) * V;
-    const float* gc = gp + (bos * s.HV + h) * K;
-    const float* bc = bp + bos * s.HV + h;
-    T* dvc_out = dvp + (bos * s.HV + h) * V;
-    float* dgc = dgp + (bos * s.HV + h) * K;
-    float* dbc = dbp + bos * s.HV + h;
+    const T* __restrict__ Sin = states + ch * K * V;
+    const T* __restrict__ dSo = reinterpret_cast<const T*>(ws.dS) + ch * K * V;
+    const T* __restrict__ yT = reinterpret_cast<const T*>(ws.yT) + ch * V * C;
+    const T* __restrict__ dOc = dOp + (bos * s.HV + h) * V;
+    const T* __restrict__ vc = vp + (bos * s.HV + h) * V;
+    const float* __restrict__ gc = gp + (bos * s.HV + h) * K;
+    const float* __restrict__ bc = bp + bos * s.HV + h;
+    const T* __restrict__ invc = invp + ch * C * C;
+    T* __restrict__ dvc_out = dvp + (bos * s.HV + h) * V;
+    float* __restrict__ dgc = dgp + (bos * s.HV + h) * K;
+    float* __restrict__ dbc = dbp + bos * s.HV + h;
 
-    if (tid < C) betas[tid] = tid < len ? bc[tid * s.HV] : 0.f;
-    for (int i = tid; i < NW * C; i += 64 * NW) dbpart[i] = 0.f;
+    // ---- phase 1: every global load of this value head
+    if (tid < C) betas[tid] = tid < len ? bc[min(tid, len - 1) * s.HV] : 0.f;
+    for (int i = tid; i < NW * C; i += NTH) dbpart[i] = 0.f;
+    float Gr[NCT][RT][4], qv[NCT][RT][4], kv[NCT][RT][4];
+#pragma unroll
+    for (int ci = 0; ci < NCT; ++ci) {
+      const int kt = wave + ci * NW;
+      if (kt < KT) {
+        col_load<float, RT>(Gr[ci], gc, gs, 16 * kt + n, grp, len);
+        col_load<T, RT>(qv[ci], qc, qs, 16 * kt + n, grp, len);
+        col_load<T, RT>(kv[ci], kc, qs, 16 * kt + n, grp, len);
+      }
+    }
+    T sraw[NCV][KT][4];
+#pragma unroll
+    for (int cv = 0; cv < NCV; ++cv) {
+      const int vt = wave + cv * NW;
+      if (vt < VT) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sraw[cv][kt][j] = Sin[(16 * kt + 4 * grp + j) * V + 16 * vt + n];
+      }
+    }
+    T invr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) invr[i] = invc[min(tid + i * NTH, C * C - 1)];
+    vecT dov[NDV];
+#pragma unroll
+    for (int i = 0; i < NDV; ++i) {
+      const int vi = min(tid + i * NTH, NVEC - 1);
+      const int row = vi / (V / VEC), c8 = vi % (V / VEC);
+      dov[i] = *reinterpret_cast<const vecT*>(dOc + min(row, len - 1) * vs + c8 * VEC);
+      if (row >= len) dov[i] = vecT{};
+    }
 
-    // ---- phase 1: gate cumsum (kept in registers), qd, kd, ki; S_in^T; INV, INV^T
-    float Gr[NCT][RT][4], gam[NCT];
+    // ---- phase 1 compute: gate cumsum, decayed q/k (row-major), S_in^T, INV, INV^T
+    float gam[NCT];
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
       const int kt = wave + ci * NW;
       gam[ci] = 0.f;
       if (kt < KT) {
         const int col = 16 * kt + n;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = 16 * rt + 4 * grp + j;
-            Gr[ci][rt][j] = row < len ? gc[row * gs + col] : 0.f;
-          }
         col_prefix<RT>(Gr[ci], lane);
         gam[ci] = __shfl(Gr[ci][RT - 1][3], n + 48, 64);
 #pragma unroll
@@ -341,36 +375,36 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * rt + 4 * grp + j;
-            const int off = row * qs + col;
-            const float kv = row < len ? to_f(kc[off]) : 0.f;
-            const float qv = row < len ? to_f(qc[off]) : 0.f;
             const float eG = __expf(Gr[ci][rt][j]);
-            Qd[row * LDK + col] = from_f<T>(s.scale * qv * eG);
-            Kd[row * LDK + col] = from_f<T>(kv * eG);
-            Ki[row * LDK + col] = from_f<T>(kv * __expf(-Gr[ci][rt][j]));
+            Qd[row * LDK + col] = from_f<T>(s.scale * qv[ci][rt][j] * eG);
+            Kd[row * LDK + col] = from_f<T>(kv[ci][rt][j] * eG);
+            Ki[row * LDK + col] = from_f<T>(kv[ci][rt][j] * __expf(-Gr[ci][rt][j]));
           }
       }
     }
-    for (int vt = wave; vt < VT; vt += NW) {
-      const int col = 16 * vt + n;
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        f32x4 s4;
+    for (int cv = 0; cv < NCV; ++cv) {
+      const int vt = wave + cv * NW;
+      if (vt < VT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s4[j] = to_f(Sin[(16 * kt + 4 * grp + j) * V + col]);
-        st4(SinT + col * LDK + 16 * kt + 4 * grp, s4);
+        for (int kt = 0; kt < KT; ++kt)
+          st4(SinT + (16 * vt + n) * LDK + 16 * kt + 4 * grp,
+              f32x4{to_f(sraw[cv][kt][0]), to_f(sraw[cv][kt][1]), to_f(sraw[cv][kt][2]), to_f(sraw[cv][kt][3])});
       }
     }
-    for (int idx = tid; idx < C * C; idx += 64 * NW) {
-      const int i = idx / C, j = idx % C;
-      const float val = (i < len && j < len) ? to_f(invp[ch * C * C + idx]) : (i == j ? 1.f : 0.f);
-      const T vt = from_f<T>(val);
-      INVt[i * LDC + j] = vt;
-      INVTt[j * LDC + i] = vt;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = tid + i * NTH;
+      if (idx < C * C) {
+        const int r = idx / C, cc = idx % C;
+        const T val = (r < len && cc < len) ? invr[i] : from_f<T>(r == cc ? 1.f : 0.f);
+        INVt[r * LDC + cc] = val;
+        INVTt[cc * LDC + r] = val;
+      }
     }
     __syncthreads();
 
-    // ---- Mqk = tril(qd ki^T) -> Mqk^T
+    // ---- Mqk = tril(qd ki^T) -> Mqk^T; F = kd ki^T (registers, same tile walk as dL below)
     block_gemm<T, RT, RT, 1, NW, K>(
         Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
         [&](int, int mt, int nt0, f32x4(&acc)[1]) {
@@ -379,10 +413,21 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
           for (int j = 0; j < 4; ++j) m4[j] = (16 * nt0 + n <= 16 * mt + 4 * grp + j) ? acc[0][j] : 0.f;
           st4(MqkT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, m4);
         }, wave, lane);
+    f32x4 Ft[NITC];
+    block_gemm<T, RT, RT, 1, NW, K>(
+        Kd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
+        [&](int it, int, int, f32x4(&acc)[1]) { Ft[it] = acc[0]; }, wave, lane);
     // ---- kd S_in -> vc0 = v - kd S_in (registers), vcorr^T = (beta vc0)^T
     f32x4 vc0[NIT1][BN1];
     block_gemm<T, RT, VT, BN1, NW, K>(Kd, LDK, 1 << 30, SinT, LDK, FullRange(),
                                       [&](int it, int mt, int nt0, f32x4(&acc)[BN1]) {
+                                        T vraw[BN1][4];
+#pragma unroll
+                                        for (int jb = 0; jb < BN1; ++jb)
+#pragma unroll
+                                          for (int j = 0; j < 4; ++j)
+                                            vraw[jb][j] = vc[min(16 * mt + 4 * grp + j, len - 1) * vs +
+                                                             16 * (nt0 + jb) + n];
 #pragma unroll
                                         for (int jb = 0; jb < BN1; ++jb) {
                                           const int col = 16 * (nt0 + jb) + n;
@@ -390,9 +435,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 #pragma unroll
                                           for (int j = 0; j < 4; ++j) {
                                             const int row = 16 * mt + 4 * grp + j;
-                                            const float vv =
-                                                row < len ? to_f(vc[row * vs + col]) : 0.f;
-                                            r[j] = vv - acc[jb][j];
+                                            r[j] = (row < len ? to_f(vraw[jb][j]) : 0.f) - acc[jb][j];
                                             b4[j] = betas[row] * r[j];
                                           }
                                           vc0[it][jb] = r;
@@ -401,7 +444,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
                                       }, wave, lane);
     __syncthreads();
 
-    // ---- qd^T, kd^T, ki^T (region A, over the dead Qd/Kd/Ki/S_in^T)
+    // ---- qd^T, kd^T, ki^T (region A, over the dead Qd/Kd/Ki/S_in^T); dO^T
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
       const int kt = wave + ci * NW;
@@ -412,19 +455,24 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
           f32x4 q4, kd4, ki4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int row = 16 * rt + 4 * grp + j;
-            const int off = row * qs + col;
-            const float kv = row < len ? to_f(kc[off]) : 0.f;
-            const float qv = row < len ? to_f(qc[off]) : 0.f;
             const float eG = __expf(Gr[ci][rt][j]);
-            q4[j] = s.scale * qv * eG;
-            kd4[j] = kv * eG;
-            ki4[j] = kv * __expf(-Gr[ci][rt][j]);
+            q4[j] = s.scale * qv[ci][rt][j] * eG;
+            kd4[j] = kv[ci][rt][j] * eG;
+            ki4[j] = kv[ci][rt][j] * __expf(-Gr[ci][rt][j]);
           }
           st4(QdT + col * LDC + 16 * rt + 4 * grp, q4);
           st4(KdT + col * LDC + 16 * rt + 4 * grp, kd4);
           st4(KiT + col * LDC + 16 * rt + 4 * grp, ki4);
         }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NDV; ++i) {
+      const int vi = tid + i * NTH;
+      if (vi < NVEC) {
+        const int row = vi / (V / VEC), c8 = vi % (V / VEC);
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) DoT[(c8 * VEC + t) * LDC + row] = dov[i][t];
       }
     }
     // ---- U = INV vcorr (row-major)
@@ -436,36 +484,30 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 #pragma unroll
             for (int j = 0; j < 4; ++j) U[(16 * mt + 4 * grp + j) * LDV + 16 * (nt0 + jb) + n] = from_f<T>(acc[jb][j]);
         }, wave, lane);
-    // ---- dO^T
-    for (int vt = wave; vt < VT; vt += NW) {
-      const int col = 16 * vt + n;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4 d4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 16 * rt + 4 * grp + j;
-          d4[j] = row < len ? to_f(dOc[row * vs + col]) : 0.f;
-        }
-        st4(DoT + col * LDC + 16 * rt + 4 * grp, d4);
-      }
-    }
     __syncthreads();
 
     // ---- dU = Mqk^T dO + kr dS -> dU^T
-    const T* yT = reinterpret_cast<const T*>(ws.yT) + ch * V * C;
     block_gemm<T, RT, VT, BN1, NW, C>(
         MqkT, LDC, 1 << 30, DoT, LDC, [](int mt, int, int& kb, int& ke) { kb = round_dn<T>(16 * mt); },
         [&](int, int mt, int nt0, f32x4(&acc)[BN1]) {
+          f32x4 y[BN1];
 #pragma unroll
-          for (int jb = 0; jb < BN1; ++jb) {
-            const int col = 16 * (nt0 + jb) + n;
-            st4(DuT + col * LDC + 16 * mt + 4 * grp, acc[jb] + ld4f(yT + col * C + 16 * mt + 4 * grp));
-          }
+          for (int jb = 0; jb < BN1; ++jb) y[jb] = ld4f(yT + (16 * (nt0 + jb) + n) * C + 16 * mt + 4 * grp);
+#pragma unroll
+          for (int jb = 0; jb < BN1; ++jb)
+            st4(DuT + (16 * (nt0 + jb) + n) * LDC + 16 * mt + 4 * grp, acc[jb] + y[jb]);
         }, wave, lane);
     __syncthreads();
 
-    // ---- dvc = INV^T dU -> -dvc (row-major), dv, dbeta part 1
+    // ---- dO row-major (into the dead dO^T slot); dvc = INV^T dU -> -dvc, dv, dbeta part 1
+#pragma unroll
+    for (int i = 0; i < NDV; ++i) {
+      const int vi = tid + i * NTH;
+      if (vi < NVEC) {
+        const int row = vi / (V / VEC), c8 = vi % (V / VEC);
+        *reinterpret_cast<vecT*>(DoR + row * LDV + c8 * VEC) = dov[i];
+      }
+    }
     block_gemm<T, RT, VT, BN1, NW, C>(
         INVTt, LDC, 1 << 30, DuT, LDC, [](int mt, int, int& kb, int& ke) { kb = round_dn<T>(16 * mt); },
         [&](int it, int mt, int nt0, f32x4(&acc)[BN1]) {
@@ -490,9 +532,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         }, wave, lane);
     __syncthreads();
 
-    // ---- dMqk = tril(dO U^T), dL = strict_tril(-dvc U^T); row-major and transposed copies
+    // ---- dMqk = tril(dO U^T); dL = strict_tril(-dvc U^T) and dbeta part 2 = rowsum(dL o (kd ki^T))
     block_gemm<T, RT, RT, 1, NW, V>(
-        dOc, vs, len, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
+        DoR, LDV, 1 << 30, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
         [&](int, int mt, int nt0, f32x4(&acc)[1]) {
           f32x4 m4;
 #pragma unroll
@@ -505,16 +547,23 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         }, wave, lane);
     block_gemm<T, RT, RT, 1, NW, V>(
         Ndv, LDV, 1 << 30, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
-        [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+        [&](int it, int mt, int nt0, f32x4(&acc)[1]) {
           f32x4 b4;
+          float part[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
             const float l = col < row ? acc[0][j] : 0.f;
             DL[row * LDC + col] = from_f<T>(l);
             b4[j] = betas[row] * l;
+            part[j] = l * Ft[it][j];
           }
           st4(BDLT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, b4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p = row_allsum16(part[j]);
+            if (n == 0) dbpart[wave * C + 16 * mt + 4 * grp + j] += p;
+          }
         }, wave, lane);
     __syncthreads();
 
@@ -524,37 +573,24 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       const int kt = wave + ci * NW;
       if (kt < KT) {
         const int col = 16 * kt + n;
-        f32x4 aq[RT], az[RT], av[RT], ai[RT], ar[RT];
+        typename M::frag bs[NKV], bd[NKV];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) aq[rt] = az[rt] = av[rt] = ai[rt] = ar[rt] = zero4();
-        float rsum = 0.f;  // this lane's share of sum_v dS[k][v] S_in[k][v], k = col
-#pragma unroll 1
-        for (int kk = 0; kk < V; kk += M::KS) {
-          const typename M::frag bs = frag_ld<T>(Sin, V, 16 * kt, kk, lane);
-          const typename M::frag bd = frag_ld<T>(dSo, V, 16 * kt, kk, lane);
-          if constexpr (M::PER == 8) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) rsum += (float)bs[i] * (float)bd[i];
-          } else {
-            rsum += bs * bd;
-          }
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            aq[rt] = M::mma(frag_ld<T>(dOc, vs, 16 * rt, kk, lane, V, len), bs, aq[rt]);
-            av[rt] = M::mma(frag_ld<T>(Ndv, LDV, 16 * rt, kk, lane), bs, av[rt]);
-            ar[rt] = M::mma(frag_ld<T>(U, LDV, 16 * rt, kk, lane), bd, ar[rt]);
-          }
+        for (int kk = 0; kk < NKV; ++kk) {
+          bs[kk] = frag_ld<T>(Sin, V, 16 * kt, kk * M::KS, lane);
+          bd[kk] = frag_ld<T>(dSo, V, 16 * kt, kk * M::KS, lane);
         }
+        f32x4 aq[RT], akd[RT], ai[RT], ar[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) aq[rt] = akd[rt] = ai[rt] = ar[rt] = zero4();
+        // triangle products first (LDS only), while the S_in / dS fragments arrive
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int klo = min(C, round_up<T>(16 * (rt + 1)));
-#pragma unroll 1
           for (int kk = 0; kk < klo; kk += M::KS) {
             const typename M::frag b = frag_ld<T>(KiT, LDC, 16 * kt, kk, lane, C, 1 << 30);
             aq[rt] = M::mma(frag_ld<T>(DMqk, LDC, 16 * rt, kk, lane, C, 1 << 30), b, aq[rt]);
-            az[rt] = M::mma(frag_ld<T>(DL, LDC, 16 * rt, kk, lane, C, 1 << 30), b, az[rt]);
+            akd[rt] = M::mma(frag_ld<T>(DL, LDC, 16 * rt, kk, lane, C, 1 << 30), b, akd[rt]);
           }
-#pragma unroll 1
           for (int kk = round_dn<T>(16 * rt); kk < C; kk += M::KS) {
             ai[rt] = M::mma(frag_ld<T>(DMqkT, LDC, 16 * rt, kk, lane, C, 1 << 30),
                             frag_ld<T>(QdT, LDC, 16 * kt, kk, lane, C, 1 << 30), ai[rt]);
@@ -562,37 +598,40 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
                             frag_ld<T>(KdT, LDC, 16 * kt, kk, lane, C, 1 << 30), ai[rt]);
           }
         }
+        float rsum = 0.f;  // this lane's share of sum_v dS[k][v] S_in[k][v], k = col
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) {
+          if constexpr (M::PER == 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) rsum += (float)bs[kk][i] * (float)bd[kk][i];
+          } else {
+            rsum += bs[kk] * bd[kk];
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            aq[rt] = M::mma(frag_ld<T>(DoR, LDV, 16 * rt, kk * M::KS, lane), bs[kk], aq[rt]);
+            akd[rt] = M::mma(frag_ld<T>(Ndv, LDV, 16 * rt, kk * M::KS, lane), bs[kk], akd[rt]);
+            ar[rt] = M::mma(frag_ld<T>(U, LDV, 16 * rt, kk * M::KS, lane), bd[kk], ar[rt]);
+          }
+        }
         rsum = col_allsum(rsum);
         const float g_last = gam[ci];
         float dG[RT][4];
         float krd = 0.f;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          float dbz[4];
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * rt + 4 * grp + j;
-            const int off = row * qs + col;
-            const float kv = row < len ? to_f(kc[off]) : 0.f;
-            const float qv = row < len ? to_f(qc[off]) : 0.f;
             const float G = Gr[ci][rt][j];
             const float eG = __expf(G), emG = __expf(-G), erG = __expf(g_last - G);
-            const float Z = az[rt][j];
-            const float dkd = betas[row] * (Z + av[rt][j]);
             const float dq_e = s.scale * eG * aq[rt][j];
-            const float dk_d = eG * dkd, dk_i = emG * ai[rt][j], dk_r = erG * ar[rt][j];
+            const float dk_d = eG * betas[row] * akd[rt][j], dk_i = emG * ai[rt][j], dk_r = erG * ar[rt][j];
             dqa[ci][rt][j] += dq_e;
             dka[ci][rt][j] += dk_d + dk_i + dk_r;
-            dG[rt][j] = qv * dq_e + kv * (dk_d - dk_i - dk_r);
-            krd += kv * dk_r;
-            dbz[j] = kv * eG * Z;
+            dG[rt][j] = qv[ci][rt][j] * dq_e + kv[ci][rt][j] * (dk_d - dk_i - dk_r);
+            krd += kv[ci][rt][j] * dk_r;
           }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p = row_allsum16(dbz[j]);
-            if (n == 0) dbpart[wave * C + 16 * rt + 4 * grp + j] += p;
-          }
-        }
         krd = col_allsum(krd);
         // dgam enters at the chunk's last valid row
         const int rl = len - 1;
@@ -623,8 +662,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     __syncthreads();
   }
 
-  T* dqc = dqp + (bos * s.H + hq) * K;
-  T* dkc = dkp + (bos * s.H + hq) * K;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, grp = lane >> 4;
+  const int len = geo.len;
+  T* __restrict__ dqc = dqp + (bos * s.H + hq) * K;
+  T* __restrict__ dkc = dkp + (bos * s.H + hq) * K;
 #pragma unroll
   for (int ci = 0; ci < NCT; ++ci) {
     const int kt = wave + ci * NW;
@@ -636,9 +677,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * rt + 4 * grp + j;
           if (row < len) {
-            const int off = row * qs + col;
-            dqc[off] = from_f<T>(dqa[ci][rt][j]);
-            dkc[off] = from_f<T>(dka[ci][rt][j]);
+            dqc[row * qs + col] = from_f<T>(dqa[ci][rt][j]);
+            dkc[row * qs + col] = from_f<T>(dka[ci][rt][j]);
           }
         }
     }
