@@ -23,6 +23,13 @@
 
 namespace kda {
 
+#ifdef KDA_PHASE_TIMING
+__device__ unsigned long long kda_phase_ts[3][8][64];
+extern "C" __attribute__((visibility("default"))) int kda_phase_ts_read(void* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(kda_phase_ts), sizeof(kda_phase_ts), 0, hipMemcpyDeviceToHost);
+}
+#endif
+
 template <class T, int K, int V, int C>
 struct BwdPrepLds {
   static constexpr int NW = 8;
@@ -78,6 +85,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
   T* __restrict__ krg = reinterpret_cast<T*>(ws.kr) + ch * C * K;
   float* __restrict__ egc = ws.eg + ch * K;
 
+  KDA_TS(0, 0);
   // ---- every global load of the chunk, issued before any use
   if (tid < C) betas[tid] = tid < len ? bc[min(tid, len - 1) * s.HV] : 0.f;
   float G[NCK][RT][4], qv[NCK][RT][4], kv[NCK][RT][4], dov[NCV][RT][4];
@@ -153,6 +161,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
   }
   __syncthreads();
 
+  KDA_TS(0, 1);
   // Mqk = tril(qd ki^T), row-major.
   block_gemm<T, RT, RT, 1, NW, K>(
       Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
@@ -181,6 +190,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
         }
       }, wave, lane);
   __syncthreads();
+  KDA_TS(0, 2);
   // Q' = qd - Mqk w, transposed.
   block_gemm<T, RT, KT, BNK, NW, C>(
       Mqk, LDC, 1 << 30, WT, LDC, [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
@@ -195,6 +205,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
         }
       }, wave, lane);
   __syncthreads();
+  KDA_TS(0, 3);
   // W = Q'^T dO, stored transposed [V][K].
   T* __restrict__ bcT = reinterpret_cast<T*>(ws.bcT) + ch * V * K;
   constexpr int BNV = VT % 2 == 0 ? 2 : 1;
@@ -208,6 +219,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
                                           st4(bcT + (16 * (nt0 + jb) + n) * K + 16 * mt + 4 * grp, acc[jb]);
                                         }
                                     }, wave, lane);
+  KDA_TS(0, 4);
 }
 
 // LDS plan of the gradient kernel. Phase-2 temporaries alias buffers that are written
@@ -234,7 +246,9 @@ struct GradLds {
   static constexpr size_t oBeta = oMqkT + szCC;
   static constexpr size_t oDbp = oBeta + sizeof(float) * C;
   static constexpr size_t oDoT = oDbp + sizeof(float) * NW * C;
-  static constexpr size_t total = oDoT + szVC;
+  // dg leaves through the dO slot in passes of SR rows of K fp32 (row stride K + 4)
+  static constexpr int SR = C < 32 ? C : 32;
+  static constexpr size_t total = mx(oDoT + szVC, oDoT + sizeof(float) * SR * (K + 4));
   static_assert(total <= 160 * 1024, "gradient kernel exceeds the LDS of one CU");
 };
 
@@ -243,7 +257,7 @@ struct GradLds {
 // global loads before using any of them; q, k and the gate cumsum G stay in registers
 // for the whole value head, and dO is read from HBM once (as 16-byte row vectors) and
 // staged in LDS transposed (for dU) and then row-major (for dMqk and dq).
-template <class T, int K, int V, int C>
+template <class T, int K, int V, int C, bool GVA>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
                                                         const T* __restrict__ vp, const float* __restrict__ gp,
                                                         const float* __restrict__ bp, const T* __restrict__ states,
@@ -294,10 +308,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
   const int qs = s.H * K, gs = s.HV * K, vs = s.HV * V;
   const T* __restrict__ qc = qp + (bos * s.H + hq) * K;
   const T* __restrict__ kc = kp + (bos * s.H + hq) * K;
+  T* __restrict__ dqc = dqp + (bos * s.H + hq) * K;
+  T* __restrict__ dkc = dkp + (bos * s.H + hq) * K;
 
-  float dqa[NCT][RT][4], dka[NCT][RT][4];
+  // Grouped heads sum dq, dk over the group in registers; otherwise they are stored
+  // directly from phase 3.
+  constexpr int NACC = GVA ? NCT : 1;
+  float dqa[NACC][RT][4], dka[NACC][RT][4];
 #pragma unroll
-  for (int ci = 0; ci < NCT; ++ci)
+  for (int ci = 0; ci < NACC; ++ci)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -324,7 +343,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     float* __restrict__ dgc = dgp + (bos * s.HV + h) * K;
     float* __restrict__ dbc = dbp + bos * s.HV + h;
 
-    // ---- phase 1: every global load of this value head
+    KDA_TS(2, 0);
+    // ---- phase 1: every global load of this value head, issued before any use
     if (tid < C) betas[tid] = tid < len ? bc[min(tid, len - 1) * s.HV] : 0.f;
     for (int i = tid; i < NW * C; i += NTH) dbpart[i] = 0.f;
     float Gr[NCT][RT][4], qv[NCT][RT][4], kv[NCT][RT][4];
@@ -337,20 +357,19 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         col_load<T, RT>(kv[ci], kc, qs, 16 * kt + n, grp, len);
       }
     }
-    T sraw[NCV][KT][4];
+    // S_in as 16-byte row pieces: piece i of this thread is row (pid % K), columns
+    // VEC*(pid / K) .. +VEC-1, so the lanes of a wave cover consecutive rows.
+    constexpr int NSV = (K * V / VEC + NTH - 1) / NTH;
+    vecT sv[NSV];
 #pragma unroll
-    for (int cv = 0; cv < NCV; ++cv) {
-      const int vt = wave + cv * NW;
-      if (vt < VT) {
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sraw[cv][kt][j] = Sin[(16 * kt + 4 * grp + j) * V + 16 * vt + n];
-      }
+    for (int i = 0; i < NSV; ++i) {
+      const int pid = min(tid + i * NTH, K * V / VEC - 1);
+      sv[i] = *reinterpret_cast<const vecT*>(Sin + (pid % K) * V + (pid / K) * VEC);
     }
-    T invr[NI];
+    constexpr int NIV = (C * C / VEC + NTH - 1) / NTH;
+    vecT iv[NIV];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) invr[i] = invc[min(tid + i * NTH, C * C - 1)];
+    for (int i = 0; i < NIV; ++i) iv[i] = *reinterpret_cast<const vecT*>(invc + min(tid + i * NTH, C * C / VEC - 1) * VEC);
     vecT dov[NDV];
 #pragma unroll
     for (int i = 0; i < NDV; ++i) {
@@ -359,8 +378,26 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       dov[i] = *reinterpret_cast<const vecT*>(dOc + min(row, len - 1) * vs + c8 * VEC);
       if (row >= len) dov[i] = vecT{};
     }
+    // v at the places of the C x V accumulator tiles this wave owns in the block walk of
+    // kd S_in and INV^T dU (same walk: RT x VT tiles in blocks of 1 x BN1)
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 vraw[NIT1][BN1];
+#pragma unroll
+    for (int it = 0; it < NIT1; ++it) {
+      const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
+      const int mt = blk / (VT / BN1), nt0 = (blk % (VT / BN1)) * BN1;
+#pragma unroll
+      for (int jb = 0; jb < BN1; ++jb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * mt + 4 * grp + j;
+          const T x = vc[min(row, len - 1) * vs + 16 * (nt0 + jb) + n];
+          vraw[it][jb][j] = row < len ? x : (T)0.0f;
+        }
+    }
 
-    // ---- phase 1 compute: gate cumsum, decayed q/k (row-major), S_in^T, INV, INV^T
+    // ---- phase 1 compute: gate cumsum, decayed q/k (row-major), S_in^T, v (row-major,
+    // in the dO^T slot until dO^T is written)
     float gam[NCT];
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
@@ -383,26 +420,30 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       }
     }
 #pragma unroll
-    for (int cv = 0; cv < NCV; ++cv) {
-      const int vt = wave + cv * NW;
-      if (vt < VT) {
+    for (int i = 0; i < NSV; ++i) {
+      const int pid = tid + i * NTH;
+      if (pid < K * V / VEC) {
+        const int row = pid % K, c0 = (pid / K) * VEC;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-          st4(SinT + (16 * vt + n) * LDK + 16 * kt + 4 * grp,
-              f32x4{to_f(sraw[cv][kt][0]), to_f(sraw[cv][kt][1]), to_f(sraw[cv][kt][2]), to_f(sraw[cv][kt][3])});
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int idx = tid + i * NTH;
-      if (idx < C * C) {
-        const int r = idx / C, cc = idx % C;
-        const T val = (r < len && cc < len) ? invr[i] : from_f<T>(r == cc ? 1.f : 0.f);
-        INVt[r * LDC + cc] = val;
-        INVTt[cc * LDC + r] = val;
+        for (int t = 0; t < VEC; ++t) SinT[(c0 + t) * LDK + row] = sv[i][t];
       }
     }
     __syncthreads();
+    // INV and INV^T (read first by U = INV vcorr, after the next barrier)
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) {
+      const int pid = tid + i * NTH;
+      if (pid < C * C / VEC) {
+        const int r = (pid * VEC) / C, c0 = (pid * VEC) % C;
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) {
+          const int cc = c0 + t;
+          const T val = (r < len && cc < len) ? iv[i][t] : from_f<T>(r == cc ? 1.f : 0.f);
+          INVt[r * LDC + cc] = val;
+          INVTt[cc * LDC + r] = val;
+        }
+      }
+    }
 
     // ---- Mqk = tril(qd ki^T) -> Mqk^T; F = kd ki^T (registers, same tile walk as dL below)
     block_gemm<T, RT, RT, 1, NW, K>(
@@ -413,21 +454,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
           for (int j = 0; j < 4; ++j) m4[j] = (16 * nt0 + n <= 16 * mt + 4 * grp + j) ? acc[0][j] : 0.f;
           st4(MqkT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, m4);
         }, wave, lane);
-    f32x4 Ft[NITC];
-    block_gemm<T, RT, RT, 1, NW, K>(
-        Kd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
-        [&](int it, int, int, f32x4(&acc)[1]) { Ft[it] = acc[0]; }, wave, lane);
-    // ---- kd S_in -> vc0 = v - kd S_in (registers), vcorr^T = (beta vc0)^T
-    f32x4 vc0[NIT1][BN1];
+    // ---- kd S_in -> vcorr^T = (beta (v - kd S_in))^T
     block_gemm<T, RT, VT, BN1, NW, K>(Kd, LDK, 1 << 30, SinT, LDK, FullRange(),
                                       [&](int it, int mt, int nt0, f32x4(&acc)[BN1]) {
-                                        T vraw[BN1][4];
-#pragma unroll
-                                        for (int jb = 0; jb < BN1; ++jb)
-#pragma unroll
-                                          for (int j = 0; j < 4; ++j)
-                                            vraw[jb][j] = vc[min(16 * mt + 4 * grp + j, len - 1) * vs +
-                                                             16 * (nt0 + jb) + n];
 #pragma unroll
                                         for (int jb = 0; jb < BN1; ++jb) {
                                           const int col = 16 * (nt0 + jb) + n;
@@ -435,15 +464,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 #pragma unroll
                                           for (int j = 0; j < 4; ++j) {
                                             const int row = 16 * mt + 4 * grp + j;
-                                            r[j] = (row < len ? to_f(vraw[jb][j]) : 0.f) - acc[jb][j];
+                                            r[j] = to_f(vraw[it][jb][j]) - acc[jb][j];
                                             b4[j] = betas[row] * r[j];
                                           }
-                                          vc0[it][jb] = r;
                                           st4(VcT + col * LDC + 16 * mt + 4 * grp, b4);
                                         }
                                       }, wave, lane);
     __syncthreads();
 
+    KDA_TS(2, 2);
     // ---- qd^T, kd^T, ki^T (region A, over the dead Qd/Kd/Ki/S_in^T); dO^T
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
@@ -486,6 +515,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         }, wave, lane);
     __syncthreads();
 
+    KDA_TS(2, 3);
     // ---- dU = Mqk^T dO + kr dS -> dU^T
     block_gemm<T, RT, VT, BN1, NW, C>(
         MqkT, LDC, 1 << 30, DoT, LDC, [](int mt, int, int& kb, int& ke) { kb = round_dn<T>(16 * mt); },
@@ -499,6 +529,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         }, wave, lane);
     __syncthreads();
 
+    KDA_TS(2, 4);
     // ---- dO row-major (into the dead dO^T slot); dvc = INV^T dU -> -dvc, dv, dbeta part 1
 #pragma unroll
     for (int i = 0; i < NDV; ++i) {
@@ -521,7 +552,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
               const float dvc = acc[jb][j];
               Ndv[row * LDV + col] = from_f<T>(-dvc);
               if (row < len) dvc_out[row * vs + col] = from_f<T>(betas[row] * dvc);
-              part[j] += dvc * vc0[it][jb][j];
+              part[j] += dvc * to_f(vraw[it][jb][j]);
             }
           }
 #pragma unroll
@@ -532,7 +563,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         }, wave, lane);
     __syncthreads();
 
-    // ---- dMqk = tril(dO U^T); dL = strict_tril(-dvc U^T) and dbeta part 2 = rowsum(dL o (kd ki^T))
+    KDA_TS(2, 5);
+    // ---- dMqk = tril(dO U^T); dL = strict_tril(-dvc U^T)
     block_gemm<T, RT, RT, 1, NW, V>(
         DoR, LDV, 1 << 30, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
         [&](int, int mt, int nt0, f32x4(&acc)[1]) {
@@ -549,25 +581,20 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         Ndv, LDV, 1 << 30, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
         [&](int it, int mt, int nt0, f32x4(&acc)[1]) {
           f32x4 b4;
-          float part[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
             const float l = col < row ? acc[0][j] : 0.f;
             DL[row * LDC + col] = from_f<T>(l);
             b4[j] = betas[row] * l;
-            part[j] = l * Ft[it][j];
           }
           st4(BDLT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, b4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p = row_allsum16(part[j]);
-            if (n == 0) dbpart[wave * C + 16 * mt + 4 * grp + j] += p;
-          }
         }, wave, lane);
     __syncthreads();
 
+    KDA_TS(2, 6);
     // ---- phase 3: per column tile of K, the C x K gradients of this value head
+    float dGk[NCT][RT][4];
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
       const int kt = wave + ci * NW;
@@ -619,7 +646,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         float dG[RT][4];
         float krd = 0.f;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
+          float dbz[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * rt + 4 * grp + j;
@@ -627,11 +655,23 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
             const float eG = __expf(G), emG = __expf(-G), erG = __expf(g_last - G);
             const float dq_e = s.scale * eG * aq[rt][j];
             const float dk_d = eG * betas[row] * akd[rt][j], dk_i = emG * ai[rt][j], dk_r = erG * ar[rt][j];
-            dqa[ci][rt][j] += dq_e;
-            dka[ci][rt][j] += dk_d + dk_i + dk_r;
+            if constexpr (GVA) {
+              dqa[ci][rt][j] += dq_e;
+              dka[ci][rt][j] += dk_d + dk_i + dk_r;
+            } else if (row < len) {
+              dqc[row * qs + col] = from_f<T>(dq_e);
+              dkc[row * qs + col] = from_f<T>(dk_d + dk_i + dk_r);
+            }
             dG[rt][j] = qv[ci][rt][j] * dq_e + kv[ci][rt][j] * (dk_d - dk_i - dk_r);
             krd += kv[ci][rt][j] * dk_r;
+            dbz[j] = kv[ci][rt][j] * eG * akd[rt][j];  // dbeta part 2: rowsum(kd o akd)
           }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p = row_allsum16(dbz[j]);
+            if (n == 0) dbpart[wave * C + 16 * rt + 4 * grp + j] += p;
+          }
+        }
         krd = col_allsum(krd);
         // dgam enters at the chunk's last valid row
         const int rl = len - 1;
@@ -646,13 +686,40 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = 16 * rt + 4 * grp + j;
-            if (row < len) dgc[row * gs + col] = dG[rt][j];
+          for (int j = 0; j < 4; ++j) dGk[ci][rt][j] = dG[rt][j];
+      }
+    }
+    // dg leaves through LDS (the dO slot, dead after the products above) as whole rows:
+    // 16-byte stores, consecutive lanes on consecutive columns.
+    {
+      constexpr int SR = Lay::SR;  // rows per pass
+      constexpr int LDG = K + 4;
+      float* stg = reinterpret_cast<float*>(smem + Lay::oDoT);
+#pragma unroll
+      for (int pass = 0; pass < C / SR; ++pass) {
+        __syncthreads();
+#pragma unroll
+        for (int ci = 0; ci < NCT; ++ci) {
+          const int kt = wave + ci * NW;
+          if (kt < KT) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              if (rt * 16 >= pass * SR && rt * 16 < (pass + 1) * SR) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) stg[(16 * rt + 4 * grp + j - pass * SR) * LDG + 16 * kt + n] = dGk[ci][rt][j];
+              }
           }
+        }
+        __syncthreads();
+        for (int i = tid; i < SR * K / 4; i += NTH) {
+          const int r = i / (K / 4), c4 = (i % (K / 4)) * 4;
+          const int row = pass * SR + r;
+          if (row < len) *reinterpret_cast<f32x4*>(dgc + row * gs + c4) = *reinterpret_cast<const f32x4*>(stg + r * LDG + c4);
+        }
       }
     }
     __syncthreads();
+    KDA_TS(2, 7);
     if (tid < len) {
       float acc = 0.f;
 #pragma unroll
@@ -662,12 +729,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     __syncthreads();
   }
 
+  KDA_TS(2, 8);
+  if constexpr (!GVA) {
+    KDA_TS(2, 9);
+    return;
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, grp = lane >> 4;
   const int len = geo.len;
-  T* __restrict__ dqc = dqp + (bos * s.H + hq) * K;
-  T* __restrict__ dkc = dkp + (bos * s.H + hq) * K;
 #pragma unroll
-  for (int ci = 0; ci < NCT; ++ci) {
+  for (int ci = 0; ci < NACC; ++ci) {
     const int kt = wave + ci * NW;
     if (kt < KT) {
       const int col = 16 * kt + n;
@@ -683,6 +753,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         }
     }
   }
+  KDA_TS(2, 9);
 }
 
 template <class T, int K, int V, int C>
@@ -707,10 +778,18 @@ static hipError_t bwd_grad_t(const Shape& s, const void* q, const void* k, const
                              const float* beta, const void* states, const void* inv, const void* dO, const BwdWs& ws,
                              void* dq, void* dk, void* dv, float* dg, float* dbeta, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_grad_kernel<T, K, V, C>), dim3(s.NT, s.H), dim3(64 * GradLds<T, K, V, C>::NW), 0, st, s, static_cast<const T*>(q),
-                     static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<const T*>(states),
-                     static_cast<const T*>(inv), static_cast<const T*>(dO), ws, static_cast<T*>(dq),
-                     static_cast<T*>(dk), static_cast<T*>(dv), dg, dbeta);
+  const dim3 grid(s.NT, s.H), block(64 * GradLds<T, K, V, C>::NW);
+  if (s.HV > s.H) {
+    hipLaunchKernelGGL((bwd_grad_kernel<T, K, V, C, true>), grid, block, 0, st, s, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<const T*>(states),
+                       static_cast<const T*>(inv), static_cast<const T*>(dO), ws, static_cast<T*>(dq),
+                       static_cast<T*>(dk), static_cast<T*>(dv), dg, dbeta);
+  } else {
+    hipLaunchKernelGGL((bwd_grad_kernel<T, K, V, C, false>), grid, block, 0, st, s, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<const T*>(states),
+                       static_cast<const T*>(inv), static_cast<const T*>(dO), ws, static_cast<T*>(dq),
+                       static_cast<T*>(dk), static_cast<T*>(dv), dg, dbeta);
+  }
   return hipGetLastError();
 }
 

@@ -15,6 +15,21 @@
 
 namespace kda {
 
+// Phase timestamps for performance work: compiled in only with -DKDA_PHASE_TIMING (never
+// in the shipped library). Slot [kernel][block][mark] holds wall_clock64() at a mark.
+#ifdef KDA_PHASE_TIMING
+extern __device__ unsigned long long kda_phase_ts[3][8][64];
+#define KDA_TS(K, I)                                                                        \
+  do {                                                                                      \
+    if (threadIdx.x == 0 && blockIdx.x < 8 && blockIdx.y == 0 && blockIdx.z == 0)           \
+      kda::kda_phase_ts[K][blockIdx.x][I] = wall_clock64();                                 \
+  } while (0)
+#else
+#define KDA_TS(K, I) \
+  do {               \
+  } while (0)
+#endif
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -222,6 +222,7 @@ __global__ __launch_bounds__(64) void scan_bf16_kernel(Shape s, const bf16* __re
     Ops cur;
     load(FWD ? c0 : c0 + nc - 1, cur);
     for (int ii = 0; ii < nc; ++ii) {
+      if (!FWD && ii < 63) KDA_TS(1, ii);
       const int c = FWD ? c0 + ii : c0 + nc - 1 - ii;
       const int in = min(ii + 1, nc - 1);
       Ops nxt;
