@@ -138,16 +138,21 @@ def main():
         kda.chunk_bwd_into(dims, d["q"], d["k"], d["v"], d["g"], d["beta"], fw["states"], fw["inv"], d["dO"],
                            d["dS_final"], dq, dk, dv, dg, dbeta, dh0, ws, stream=stream)
 
-    def timed(nsteps, flush):
+    def timed(nsteps, flush, per_kernel):
+        """nsteps calls; HIP events around each call on its stream, and (per_kernel) the
+        library's events around each of its kernels. The timed region is bracketed by
+        device synchronisation."""
         call_ev = new_events(2 * nsteps)
-        kern_ev = new_events(2 * nk * nsteps)
+        kern_ev = new_events(2 * nk * nsteps) if per_kernel else None
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(nsteps):
             if flush:
                 flush_buf.fill_(i & 0xFF)
-            lib.kda_set_kernel_events(ctypes.cast(ctypes.byref(kern_ev, 2 * nk * i * ctypes.sizeof(ctypes.c_void_p)),
-                                                  ctypes.POINTER(ctypes.c_void_p)), 2 * nk)
+            if per_kernel:
+                lib.kda_set_kernel_events(
+                    ctypes.cast(ctypes.byref(kern_ev, 2 * nk * i * ctypes.sizeof(ctypes.c_void_p)),
+                                ctypes.POINTER(ctypes.c_void_p)), 2 * nk)
             hip.hipEventRecord(call_ev[2 * i], stream)
             step()
             hip.hipEventRecord(call_ev[2 * i + 1], stream)
@@ -155,17 +160,21 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         calls = [elapsed(call_ev[2 * i], call_ev[2 * i + 1]) for i in range(nsteps)]
-        kern = {name: [elapsed(kern_ev[2 * nk * i + 2 * j], kern_ev[2 * nk * i + 2 * j + 1]) for i in range(nsteps)]
-                for j, name in enumerate(kernel_names)}
-        for arr in (call_ev, kern_ev):
+        kern = {}
+        if per_kernel:
+            kern = {name: [elapsed(kern_ev[2 * nk * i + 2 * j], kern_ev[2 * nk * i + 2 * j + 1])
+                           for i in range(nsteps)] for j, name in enumerate(kernel_names)}
+        for arr in (call_ev, kern_ev or []):
             for e in arr:
                 hip.hipEventDestroy(e)
         return calls, kern, wall
 
     for _ in range(args.warmup):
         step()
-    cold_calls, cold_kern, cold_wall = timed(args.steps, flush=True)
-    warm_calls, warm_kern, warm_wall = timed(args.steps, flush=False)
+    cold_calls, _, cold_wall = timed(args.steps, flush=True, per_kernel=False)
+    warm_calls, _, _ = timed(args.steps, flush=False, per_kernel=False)
+    _, cold_kern, _ = timed(args.steps, flush=True, per_kernel=True)
+    _, warm_kern, _ = timed(args.steps, flush=False, per_kernel=True)
 
     th = B * T * w.HV
     ms = statistics.mean(cold_calls)
