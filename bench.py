@@ -78,6 +78,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1, help="workload id (1 = B=2,T=2048,H=8,K=V=128,C=64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB a few times (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the KDA chunk backward here runs on a single MI355X and has no "
@@ -85,6 +88,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": args.copy_calibration << 20, "copies": 3}), flush=True)
+        return
     import chunked_gated_delta_09_amd as kda
     from chunked_gated_delta_09_amd import inputs as kin
 

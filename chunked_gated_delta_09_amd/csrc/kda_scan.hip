@@ -166,9 +166,18 @@ __global__ __launch_bounds__(64) void scan_bf16_kernel(Shape s, const bf16* __re
                                                         bf16* __restrict__ Yout, float* __restrict__ Xfin) {
   typedef ScanFrag<K, V, C> F;
   typedef Mma<bf16> M;
-  constexpr int KT = F::KT, CT = F::CT, KP = F::KP, CQ = F::CQ;
+  constexpr int KT = F::KT, CT = F::CT, KP = F::KP, CQ = F::CQ, VT = V / 16;
   static_assert(KT % 2 == 0, "the bf16 scan pairs row tiles of X");
-  const int vt = blockIdx.x, h = blockIdx.y, nseq = blockIdx.z;
+  // Workgroups are dealt round-robin to the 8 XCDs by linear id, so ids i, i+8, i+16, ...
+  // share an XCD (and its L2). All VT column slices of one (sequence, head) get ids of one
+  // residue class mod 8: the slices' shared per-chunk operands are then fetched from HBM
+  // once per XCD and served from L2 to the others.
+  const int wid = blockIdx.x;
+  const int xcd = wid % 8, r = wid / 8;
+  const int pair = (r / VT) * 8 + xcd;  // (sequence, head) index
+  const int vt = r % VT;
+  if (pair >= s.N * s.HV) return;
+  const int h = pair % s.HV, nseq = pair / s.HV;
   const int lane = threadIdx.x, n = lane & 15, grp = lane >> 4;
   const int vcol = 16 * vt + n;
   int c0, nc;
@@ -310,7 +319,9 @@ static hipError_t scan_t(const Shape& s, const void* P1, const void* P2, const v
                          const float* eg, const void* X0, void* Xout, void* Yout, float* Xfin, hipStream_t st) {
   if (s.N == 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((scan_bf16_kernel<K, V, C, FWD>), dim3(V / 16, s.HV, s.N), dim3(64), 0, st, s,
+    const int pairs = s.N * s.HV;
+    const int grid = ((pairs + 7) / 8) * 8 * (V / 16);
+    hipLaunchKernelGGL((scan_bf16_kernel<K, V, C, FWD>), dim3(grid), dim3(64), 0, st, s,
                        static_cast<const bf16*>(P1), static_cast<const bf16*>(P2), static_cast<const bf16*>(Zi),
                        static_cast<const bf16*>(Wi), eg, static_cast<const bf16*>(X0), static_cast<bf16*>(Xout),
                        static_cast<bf16*>(Yout), Xfin);
