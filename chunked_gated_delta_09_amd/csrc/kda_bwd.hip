@@ -214,7 +214,11 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
 #pragma unroll
                                       for (int jb = 0; jb < BNV; ++jb)
                                         if constexpr (sizeof(T) == 2) {
-                                          st4(bcT + ScanFrag<K, V, C>::seed(nt0 + jb, mt, KT, lane), acc[jb]);
+                                          // column v = 16(nt0 + jb) + n goes to its scan slice and lane
+                                          const int v = 16 * (nt0 + jb) + n;
+                                          st4(bcT + ScanFrag<K, V, C>::seed(ScanCols::slice(v), mt, KT,
+                                                                            ScanCols::lane_col(v) + 16 * grp),
+                                              acc[jb]);
                                         } else {
                                           st4(bcT + (16 * (nt0 + jb) + n) * K + 16 * mt + 4 * grp, acc[jb]);
                                         }
@@ -595,16 +599,31 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     KDA_TS(2, 6);
     // ---- phase 3: per column tile of K, the C x K gradients of this value head
     float dGk[NCT][RT][4];
+    // 16 x 16 identity as the B operand of a 16x16x16 bf16 MFMA (lane: column n, rows 4grp..)
+    typedef short s4i __attribute__((ext_vector_type(4)));
+    s4i ident4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ident4[j] = (4 * grp + j == n) ? (short)0x3f80 : (short)0;
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
       const int kt = wave + ci * NW;
       if (kt < KT) {
         const int col = 16 * kt + n;
+        // dS: the bf16 scan leaves its column slices' tiles as it holds them (4 rows per
+        // lane); those of slices 2kk and 2kk+1, transposed by an MFMA against the identity,
+        // form the B fragment of columns 32kk.. (done at the point of use below).
         typename M::frag bs[NKV], bd[NKV];
+        s4i dsr[NKV][2];
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
           bs[kk] = frag_ld<T>(Sin, V, 16 * kt, kk * M::KS, lane);
-          bd[kk] = frag_ld<T>(dSo, V, 16 * kt, kk * M::KS, lane);
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+              dsr[kk][b] = *reinterpret_cast<const s4i*>(dSo + ScanFrag<K, V, C>::seed(2 * kk + b, kt, KT, lane));
+          } else {
+            bd[kk] = frag_ld<T>(dSo, V, 16 * kt, kk * M::KS, lane);
+          }
         }
         f32x4 aq[RT], akd[RT], ai[RT], ar[RT];
 #pragma unroll
@@ -628,6 +647,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         float rsum = 0.f;  // this lane's share of sum_v dS[k][v] S_in[k][v], k = col
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
+          if constexpr (sizeof(T) == 2) {
+            const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsr[kk][0], ident4, zero4(), 0, 0, 0);
+            const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsr[kk][1], ident4, zero4(), 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              bd[kk][i] = (bf16)d0[i];
+              bd[kk][4 + i] = (bf16)d1[i];
+            }
+          }
           if constexpr (M::PER == 8) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) rsum += (float)bs[kk][i] * (float)bd[kk][i];

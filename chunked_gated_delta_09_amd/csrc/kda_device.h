@@ -384,6 +384,19 @@ struct ScanFrag {
   }
 };
 
+// Columns of the backward scan's column slices. Slice vt, lane column n, holds value
+// column col(vt, n): slices 2m and 2m+1 share the 32 columns 32m.., each taking 4 of every
+// 8. After a 16 x 16 transpose the 4 values a lane holds of slice 2m and those of slice
+// 2m+1 are the 8 consecutive columns 32m + 8(lane/16) .. + 7 of a B operand fragment.
+struct ScanCols {
+  __device__ __forceinline__ static int col(int vt, int n) {
+    return 32 * (vt >> 1) + 8 * (n >> 2) + 4 * (vt & 1) + (n & 3);
+  }
+  // inverse: the slice and lane column of value column v
+  __device__ __forceinline__ static int slice(int v) { return 2 * (v >> 5) + ((v & 7) >> 2); }
+  __device__ __forceinline__ static int lane_col(int v) { return 4 * ((v & 31) >> 3) + (v & 3); }
+};
+
 // Contraction-range helpers for triangular operands (K step = KS, tiles of 16 rows).
 template <class T>
 __device__ __forceinline__ int round_dn(int x) { return (x / Mma<T>::KS) * Mma<T>::KS; }

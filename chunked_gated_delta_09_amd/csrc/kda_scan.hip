@@ -157,9 +157,19 @@ __global__ __launch_bounds__(64) void scan_kernel(Shape s, const T* __restrict__
 // bf16 path: the per-chunk operands are stored in fragment order (ScanFrag), so each wave
 // load is a contiguous 1 KB block, and the next chunk's operands are loaded into registers
 // while the current chunk is computed (the index is clamped, so the loads are
-// unconditional and always in flight).
+// unconditional and always in flight). A second wave keeps the operands TOUCH_AHEAD chunks
+// further on moving into L2: one 4-byte load per 128-byte line, the lines shared by the
+// column slices of a head split between their workgroups, each load delivered into a
+// scratch word of LDS so that it holds no register and is never waited for. The two waves
+// meet at one barrier per chunk, which keeps the touches a fixed distance ahead.
+//
+// Backward direction: a column slice covers the columns ScanCols::col(vt, n) (not 16
+// consecutive ones), and the per-chunk dS leaves exactly as this wave holds it, 4 values
+// per lane and row tile in seed order (one 8-byte store per row tile); the gradient kernel
+// transposes it, and the column choice makes the transposed values of two slices one
+// contiguous B fragment.
 template <int K, int V, int C, bool FWD>
-__global__ __launch_bounds__(64) void scan_bf16_kernel(Shape s, const bf16* __restrict__ P1,
+__global__ __launch_bounds__(128) void scan_bf16_kernel(Shape s, const bf16* __restrict__ P1,
                                                         const bf16* __restrict__ P2, const bf16* __restrict__ Zs,
                                                         const bf16* __restrict__ Ws, const float* __restrict__ eg,
                                                         const bf16* __restrict__ X0, bf16* __restrict__ Xout,
@@ -178,15 +188,49 @@ __global__ __launch_bounds__(64) void scan_bf16_kernel(Shape s, const bf16* __re
   const int vt = r % VT;
   if (pair >= s.N * s.HV) return;
   const int h = pair % s.HV, nseq = pair / s.HV;
-  const int lane = threadIdx.x, n = lane & 15, grp = lane >> 4;
-  const int vcol = 16 * vt + n;
+  const int lane = threadIdx.x & 63, n = lane & 15, grp = lane >> 4;
+  const int vcol = FWD ? 16 * vt + n : ScanCols::col(vt, n);
   int c0, nc;
   seq_range(nseq, s.cu, s.choff, s.T, C, c0, nc);
   if (c0 + nc > s.NT) nc = max(0, s.NT - c0);
+  constexpr int TOUCH_AHEAD = 4;
 
-  struct Ops {
+  if (threadIdx.x >= 64) {
+    // prefetch wave: lanes 0..31 cover this slice's share of the lines of P1 and P2,
+    // lanes 32..63 the lines of this slice's own seed tiles; a second load covers e^gam.
+    constexpr int SHARED_LINES = (F::P1_ELEMS + F::P2_ELEMS) * 2 / 128;
+    constexpr int SEED_LINES = (FWD ? C : K) * 16 * 2 / 128;
+    static_assert(SHARED_LINES <= 32 * VT && SEED_LINES <= 32, "one touch covers at most 64 lines per wave");
+    __shared__ int sink[64];
+    const int tl = min(32 * vt + (lane & 31), SHARED_LINES - 1);
+    const int tl2 = max(0, min(lane - 32, SEED_LINES - 1));
+    auto touch = [&](int c) {
+      const long ch = (long)c * s.HV + h;
+      const bf16* a;
+      if (lane < 32) {
+        a = tl < F::P1_ELEMS / 64 ? P1 + ch * F::P1_ELEMS + 64 * tl : P2 + ch * F::P2_ELEMS + 64 * (tl - F::P1_ELEMS / 64);
+      } else {
+        a = (FWD ? Zs + ch * C * V + F::seed(vt, 0, CT, 0) : Ws + ch * K * V + F::seed(vt, 0, KT, 0)) + 64 * tl2;
+      }
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)a,
+                                       (__attribute__((address_space(3))) void*)sink, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(eg + ch * K + 32 * (lane % ((K + 31) / 32))),
+                                       (__attribute__((address_space(3))) void*)sink, 4, 0, 0);
+    };
+    for (int d = 1; d < TOUCH_AHEAD && d < nc; ++d) touch(FWD ? c0 + d : c0 + nc - 1 - d);
+    for (int ii = 0; ii < nc; ++ii) {
+      __builtin_amdgcn_s_barrier();
+      if (ii + TOUCH_AHEAD < nc) touch(FWD ? c0 + ii + TOUCH_AHEAD : c0 + nc - 1 - ii - TOUCH_AHEAD);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
+
+  struct Ops {  // double-buffered: the next chunk's are loaded during the current step
     bf16x8 a1[CT][KP];
     bf16x8 a2[KT][CQ];
+  };
+  struct Small {  // loaded at the start of their own step, ahead of the next chunk's Ops
     bf16x4 w[KT];
     bf16x4 z[CT];
     f32x4 e[KT];
@@ -203,6 +247,9 @@ __global__ __launch_bounds__(64) void scan_bf16_kernel(Shape s, const bf16* __re
     for (int t = 0; t < KT; ++t)
 #pragma unroll
       for (int q = 0; q < CQ; ++q) o.a2[t][q] = p2[(t * CQ + q) * 64];
+  };
+  auto load_small = [&](int c, Small& o) {
+    const long ch = (long)c * s.HV + h;
     if constexpr (!FWD) {
 #pragma unroll
       for (int t = 0; t < KT; ++t) o.w[t] = *reinterpret_cast<const bf16x4*>(Ws + ch * K * V + F::seed(vt, t, KT, lane));
@@ -227,81 +274,101 @@ __global__ __launch_bounds__(64) void scan_bf16_kernel(Shape s, const bf16* __re
     for (int t = 0; t < KT; ++t) X[t] = zero4();
   }
 
-  if (nc > 0) {
-    Ops cur;
-    load(FWD ? c0 : c0 + nc - 1, cur);
-    for (int ii = 0; ii < nc; ++ii) {
-      if (!FWD && ii < 63) KDA_TS(1, ii);
-      const int c = FWD ? c0 + ii : c0 + nc - 1 - ii;
+  // One chunk step with operands `cur`; the loads of the next chunk into `nxt` are issued
+  // first. The loop below alternates two buffers, so no register copy ever waits on a load
+  // still in flight.
+  auto step = [&](int ii, const Ops& cur, Ops& nxt) {
+    __builtin_amdgcn_s_barrier();
+    if (!FWD && ii < 63) KDA_TS(1, ii);
+    const int c = FWD ? c0 + ii : c0 + nc - 1 - ii;
+    Small sm;
+    load_small(c, sm);
+    {
       const int in = min(ii + 1, nc - 1);
-      Ops nxt;
       load(FWD ? c0 + in : c0 + nc - 1 - in, nxt);
-      const long ch = (long)c * s.HV + h;
+    }
+    const long ch = (long)c * s.HV + h;
 
+    bf16x8 bx[KP];
+#pragma unroll
+    for (int p = 0; p < KP; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bx[p][i] = (bf16)X[2 * p][i];
+        bx[p][4 + i] = (bf16)X[2 * p + 1][i];
+      }
+    if constexpr (FWD) {
       bf16* xo = Xout + ch * K * V;
 #pragma unroll
       for (int t = 0; t < KT; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xo[(16 * t + 4 * grp + j) * V + vcol] = (bf16)X[t][j];
+        for (int j = 0; j < 4; ++j) xo[(16 * t + 4 * grp + j) * V + vcol] = bx[t / 2][4 * (t % 2) + j];
+    } else {
+      bf16* xo = Xout + ch * K * V;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+        *reinterpret_cast<bf16x4*>(xo + F::seed(vt, t, KT, lane)) =
+            bf16x4{bx[t / 2][4 * (t % 2)], bx[t / 2][4 * (t % 2) + 1], bx[t / 2][4 * (t % 2) + 2], bx[t / 2][4 * (t % 2) + 3]};
+    }
 
-      // Y = Z + P1 X
-      f32x4 Y[CT];
+    // Y = Z + P1 X
+    f32x4 Y[CT];
 #pragma unroll
-      for (int m = 0; m < CT; ++m) {
-        if constexpr (FWD) {
-          Y[m] = f32x4{(float)cur.z[m][0], (float)cur.z[m][1], (float)cur.z[m][2], (float)cur.z[m][3]};
-        } else {
-          Y[m] = zero4();
-        }
+    for (int m = 0; m < CT; ++m) {
+      if constexpr (FWD) {
+        Y[m] = f32x4{(float)sm.z[m][0], (float)sm.z[m][1], (float)sm.z[m][2], (float)sm.z[m][3]};
+      } else {
+        Y[m] = zero4();
       }
+    }
 #pragma unroll
-      for (int p = 0; p < KP; ++p) {
-        bf16x8 b;
+    for (int p = 0; p < KP; ++p)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          b[i] = (bf16)X[2 * p][i];
-          b[4 + i] = (bf16)X[2 * p + 1][i];
-        }
+      for (int m = 0; m < CT; ++m) Y[m] = M::mma(cur.a1[m][p], bx[p], Y[m]);
+    if (Yout != nullptr) {
 #pragma unroll
-        for (int m = 0; m < CT; ++m) Y[m] = M::mma(cur.a1[m][p], b, Y[m]);
-      }
-      if (Yout != nullptr) {
-#pragma unroll
-        for (int m = 0; m < CT; ++m) st4(Yout + ch * V * C + vcol * C + 16 * m + 4 * grp, Y[m]);
-      }
+      for (int m = 0; m < CT; ++m) st4(Yout + ch * V * C + vcol * C + 16 * m + 4 * grp, Y[m]);
+    }
 
-      // X' = W + P2 Y;  X = diag(e^gam) X + X'
-      f32x4 Xn[KT];
+    // X' = W + P2 Y;  X = diag(e^gam) X + X'
+    f32x4 Xn[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      if constexpr (!FWD) {
+        Xn[t] = f32x4{(float)sm.w[t][0], (float)sm.w[t][1], (float)sm.w[t][2], (float)sm.w[t][3]};
+      } else {
+        Xn[t] = zero4();
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < CQ; ++q) {
+      const bool pair = 2 * q + 1 < CT;
+      bf16x8 b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        b[i] = (bf16)Y[2 * q][i];
+        b[4 + i] = pair ? (bf16)Y[pair ? 2 * q + 1 : 2 * q][i] : (bf16)0.0f;
+      }
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
-        if constexpr (!FWD) {
-          Xn[t] = f32x4{(float)cur.w[t][0], (float)cur.w[t][1], (float)cur.w[t][2], (float)cur.w[t][3]};
-        } else {
-          Xn[t] = zero4();
+        bf16x8 a = cur.a2[t][q];
+        if (!pair) {
+#pragma unroll
+          for (int i = 4; i < 8; ++i) a[i] = (bf16)0.0f;
         }
+        Xn[t] = M::mma(a, b, Xn[t]);
       }
+    }
 #pragma unroll
-      for (int q = 0; q < CQ; ++q) {
-        const bool pair = 2 * q + 1 < CT;
-        bf16x8 b;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          b[i] = (bf16)Y[2 * q][i];
-          b[4 + i] = pair ? (bf16)Y[pair ? 2 * q + 1 : 2 * q][i] : (bf16)0.0f;
-        }
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-          bf16x8 a = cur.a2[t][q];
-          if (!pair) {
-#pragma unroll
-            for (int i = 4; i < 8; ++i) a[i] = (bf16)0.0f;
-          }
-          Xn[t] = M::mma(a, b, Xn[t]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < KT; ++t) X[t] = cur.e[t] * X[t] + Xn[t];
-      cur = nxt;
+    for (int t = 0; t < KT; ++t) X[t] = sm.e[t] * X[t] + Xn[t];
+  };
+
+  if (nc > 0) {
+    Ops ping, pong;
+    load(FWD ? c0 : c0 + nc - 1, ping);
+    for (int ii = 0; ii < nc; ii += 2) {
+      step(ii, ping, pong);
+      if (ii + 1 < nc) step(ii + 1, pong, ping);
     }
   }
 
@@ -321,7 +388,7 @@ static hipError_t scan_t(const Shape& s, const void* P1, const void* P2, const v
   if constexpr (sizeof(T) == 2) {
     const int pairs = s.N * s.HV;
     const int grid = ((pairs + 7) / 8) * 8 * (V / 16);
-    hipLaunchKernelGGL((scan_bf16_kernel<K, V, C, FWD>), dim3(grid), dim3(64), 0, st, s,
+    hipLaunchKernelGGL((scan_bf16_kernel<K, V, C, FWD>), dim3(grid), dim3(128), 0, st, s,
                        static_cast<const bf16*>(P1), static_cast<const bf16*>(P2), static_cast<const bf16*>(Zi),
                        static_cast<const bf16*>(Wi), eg, static_cast<const bf16*>(X0), static_cast<bf16*>(Xout),
                        static_cast<bf16*>(Yout), Xfin);
