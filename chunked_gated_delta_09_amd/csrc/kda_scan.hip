@@ -325,7 +325,7 @@ __global__ __launch_bounds__(128) void scan_bf16_kernel(Shape s, const bf16* __r
     for (int p = 0; p < KP; ++p)
 #pragma unroll
       for (int m = 0; m < CT; ++m) Y[m] = M::mma(cur.a1[m][p], bx[p], Y[m]);
-    if (Yout != nullptr) {
+    if constexpr (!FWD) {
 #pragma unroll
       for (int m = 0; m < CT; ++m) st4(Yout + ch * V * C + vcol * C + 16 * m + 4 * grp, Y[m]);
     }
@@ -361,6 +361,17 @@ __global__ __launch_bounds__(128) void scan_bf16_kernel(Shape s, const bf16* __r
     }
 #pragma unroll
     for (int t = 0; t < KT; ++t) X[t] = sm.e[t] * X[t] + Xn[t];
+    // Issue order: this step's small loads first, then one load of the next chunk's
+    // fragments after each MFMA, so that the address unit works while the matrix pipe does
+    // (issued as one burst, the loads would hold up the MFMAs behind them).
+    constexpr int NSMALL = KT + (FWD ? CT : KT), NMMA = CT * KP + KT * CQ;
+    static_assert(NMMA == CT * KP + KT * CQ, "one next-chunk load per MFMA");
+    __builtin_amdgcn_sched_group_barrier(0x020, NSMALL, 0);
+#pragma unroll
+    for (int i = 0; i < NMMA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
   };
 
   if (nc > 0) {
