@@ -87,7 +87,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
 
   KDA_TS(0, 0);
   // ---- every global load of the chunk, issued before any use
-  if (tid < C) betas[tid] = tid < len ? bc[min(tid, len - 1) * s.HV] : 0.f;
+  const float beta_raw = bc[min(tid % C, len - 1) * s.HV];
   float G[NCK][RT][4], qv[NCK][RT][4], kv[NCK][RT][4], dov[NCV][RT][4];
 #pragma unroll
   for (int ci = 0; ci < NCK; ++ci) {
@@ -109,6 +109,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
     const int idx = tid + i * NTH;
     invr[i] = idx < C * C ? invc[idx] : (T)0.0f;
   }
+  if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
   __syncthreads();
 
   // ---- gate cumsum and the decayed keys / queries
@@ -349,17 +350,18 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 
     KDA_TS(2, 0);
     // ---- phase 1: every global load of this value head, issued before any use
-    if (tid < C) betas[tid] = tid < len ? bc[min(tid, len - 1) * s.HV] : 0.f;
+    // beta: loaded with the rest, written to LDS once everything is in flight
+    const float beta_raw = bc[min(tid % C, len - 1) * s.HV];
     for (int i = tid; i < NW * C; i += NTH) dbpart[i] = 0.f;
     float Gr[NCT][RT][4], qv[NCT][RT][4], kv[NCT][RT][4];
+    ColTile<float, RT> tg[NCT];
+    ColTile<T, RT> tq[NCT], tk[NCT];
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
-      const int kt = wave + ci * NW;
-      if (kt < KT) {
-        col_load<float, RT>(Gr[ci], gc, gs, 16 * kt + n, grp, len);
-        col_load<T, RT>(qv[ci], qc, qs, 16 * kt + n, grp, len);
-        col_load<T, RT>(kv[ci], kc, qs, 16 * kt + n, grp, len);
-      }
+      const int kt = min(wave + ci * NW, KT - 1);  // clamped: loads stay unconditional
+      tg[ci].load(gc, gs, 16 * kt, lane, len);
+      tq[ci].load(qc, qs, 16 * kt, lane, len);
+      tk[ci].load(kc, qs, 16 * kt, lane, len);
     }
     // S_in as 16-byte row pieces: piece i of this thread is row (pid % K), columns
     // VEC*(pid / K) .. +VEC-1, so the lanes of a wave cover consecutive rows.
@@ -386,22 +388,49 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     // kd S_in and INV^T dU (same walk: RT x VT tiles in blocks of 1 x BN1)
     typedef T t4 __attribute__((ext_vector_type(4)));
     t4 vraw[NIT1][BN1];
+    ColTile<T, 1> tv[NIT1][BN1];
+#pragma unroll
+    for (int it = 0; it < NIT1; ++it) {
+      const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
+      const int mt = blk / (VT / BN1), nt0 = (blk % (VT / BN1)) * BN1;
+#pragma unroll
+      for (int jb = 0; jb < BN1; ++jb) tv[it][jb].load(vc, vs, 16 * (nt0 + jb), lane, len, 16 * mt);
+    }
+    // (kr dS)^T at the places of the dU tiles this wave owns (same block walk), for the dU
+    // epilogue
+    t4 yraw[NIT1][BN1];
 #pragma unroll
     for (int it = 0; it < NIT1; ++it) {
       const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
       const int mt = blk / (VT / BN1), nt0 = (blk % (VT / BN1)) * BN1;
 #pragma unroll
       for (int jb = 0; jb < BN1; ++jb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 16 * mt + 4 * grp + j;
-          const T x = vc[min(row, len - 1) * vs + 16 * (nt0 + jb) + n];
-          vraw[it][jb][j] = row < len ? x : (T)0.0f;
-        }
+        yraw[it][jb] = *reinterpret_cast<const t4*>(yT + (16 * (nt0 + jb) + n) * C + 16 * mt + 4 * grp);
     }
 
-    // ---- phase 1 compute: gate cumsum, decayed q/k (row-major), S_in^T, v (row-major,
-    // in the dO^T slot until dO^T is written)
+    // ---- phase 1 compute: column tiles of g, q, k and v into the column-owner layout; gate
+    // cumsum, decayed q/k (row-major), S_in^T
+    if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
+#pragma unroll
+    for (int ci = 0; ci < NCT; ++ci) {
+      if (wave + ci * NW < KT) {
+        tg[ci].get(Gr[ci], lane, len);
+        tq[ci].get(qv[ci], lane, len);
+        tk[ci].get(kv[ci], lane, len);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT1; ++it) {
+      const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
+      const int mt = blk / (VT / BN1);
+#pragma unroll
+      for (int jb = 0; jb < BN1; ++jb) {
+        float x[1][4];
+        tv[it][jb].get(x, lane, len, 16 * mt);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vraw[it][jb][j] = from_f<T>(x[0][j]);
+      }
+    }
     float gam[NCT];
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
@@ -412,15 +441,31 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         col_prefix<RT>(Gr[ci], lane);
         gam[ci] = __shfl(Gr[ci][RT - 1][3], n + 48, 64);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4 q4, kd4, ki4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int row = 16 * rt + 4 * grp + j;
             const float eG = __expf(Gr[ci][rt][j]);
-            Qd[row * LDK + col] = from_f<T>(s.scale * qv[ci][rt][j] * eG);
-            Kd[row * LDK + col] = from_f<T>(kv[ci][rt][j] * eG);
-            Ki[row * LDK + col] = from_f<T>(kv[ci][rt][j] * __expf(-Gr[ci][rt][j]));
+            q4[j] = s.scale * qv[ci][rt][j] * eG;
+            kd4[j] = kv[ci][rt][j] * eG;
+            ki4[j] = kv[ci][rt][j] * __expf(-Gr[ci][rt][j]);
           }
+          if constexpr (sizeof(T) == 2) {
+            // row layout (this lane: row 16rt + n, columns 16kt + 4grp ..): 8-byte writes
+            const int off = (16 * rt + n) * LDK + 16 * kt + 4 * grp;
+            st4(Qd + off, to_rows_bf16(q4[0], q4[1], q4[2], q4[3], lane));
+            st4(Kd + off, to_rows_bf16(kd4[0], kd4[1], kd4[2], kd4[3], lane));
+            st4(Ki + off, to_rows_bf16(ki4[0], ki4[1], ki4[2], ki4[3], lane));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int row = 16 * rt + 4 * grp + j;
+              Qd[row * LDK + col] = from_f<T>(q4[j]);
+              Kd[row * LDK + col] = from_f<T>(kd4[j]);
+              Ki[row * LDK + col] = from_f<T>(ki4[j]);
+            }
+          }
+        }
       }
     }
 #pragma unroll
@@ -433,6 +478,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       }
     }
     __syncthreads();
+    KDA_TS(2, 1);
     // INV and INV^T (read first by U = INV vcorr, after the next barrier)
 #pragma unroll
     for (int i = 0; i < NIV; ++i) {
@@ -523,13 +569,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     // ---- dU = Mqk^T dO + kr dS -> dU^T
     block_gemm<T, RT, VT, BN1, NW, C>(
         MqkT, LDC, 1 << 30, DoT, LDC, [](int mt, int, int& kb, int& ke) { kb = round_dn<T>(16 * mt); },
-        [&](int, int mt, int nt0, f32x4(&acc)[BN1]) {
-          f32x4 y[BN1];
+        [&](int it, int mt, int nt0, f32x4(&acc)[BN1]) {
 #pragma unroll
-          for (int jb = 0; jb < BN1; ++jb) y[jb] = ld4f(yT + (16 * (nt0 + jb) + n) * C + 16 * mt + 4 * grp);
-#pragma unroll
-          for (int jb = 0; jb < BN1; ++jb)
-            st4(DuT + (16 * (nt0 + jb) + n) * LDC + 16 * mt + 4 * grp, acc[jb] + y[jb]);
+          for (int jb = 0; jb < BN1; ++jb) {
+            const f32x4 y = {to_f(yraw[it][jb][0]), to_f(yraw[it][jb][1]), to_f(yraw[it][jb][2]), to_f(yraw[it][jb][3])};
+            st4(DuT + (16 * (nt0 + jb) + n) * LDC + 16 * mt + 4 * grp, acc[jb] + y);
+          }
         }, wave, lane);
     __syncthreads();
 
@@ -568,6 +613,29 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     __syncthreads();
 
     KDA_TS(2, 5);
+    // The S_in and dS fragments of phase 3 (column tile kt of this wave): issued here so that
+    // they arrive during the two products below. dS: the bf16 scan leaves its column slices'
+    // tiles as it holds them (4 rows per lane); those of slices 2kk and 2kk+1, transposed by
+    // an MFMA against the identity, form the B fragment of columns 32kk.. (done at the point
+    // of use in phase 3).
+    typedef short s4i __attribute__((ext_vector_type(4)));
+    typename M::frag bs[NCT][NKV], bd[NCT][NKV];
+    s4i dsr[NCT][NKV][2];
+#pragma unroll
+    for (int ci = 0; ci < NCT; ++ci) {
+      const int kt = min(wave + ci * NW, KT - 1);
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk) {
+        bs[ci][kk] = frag_ld<T>(Sin, V, 16 * kt, kk * M::KS, lane);
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            dsr[ci][kk][b] = *reinterpret_cast<const s4i*>(dSo + ScanFrag<K, V, C>::seed(2 * kk + b, kt, KT, lane));
+        } else {
+          bd[ci][kk] = frag_ld<T>(dSo, V, 16 * kt, kk * M::KS, lane);
+        }
+      }
+    }
     // ---- dMqk = tril(dO U^T); dL = strict_tril(-dvc U^T)
     block_gemm<T, RT, RT, 1, NW, V>(
         DoR, LDV, 1 << 30, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
@@ -600,7 +668,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     // ---- phase 3: per column tile of K, the C x K gradients of this value head
     float dGk[NCT][RT][4];
     // 16 x 16 identity as the B operand of a 16x16x16 bf16 MFMA (lane: column n, rows 4grp..)
-    typedef short s4i __attribute__((ext_vector_type(4)));
     s4i ident4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) ident4[j] = (4 * grp + j == n) ? (short)0x3f80 : (short)0;
@@ -609,22 +676,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       const int kt = wave + ci * NW;
       if (kt < KT) {
         const int col = 16 * kt + n;
-        // dS: the bf16 scan leaves its column slices' tiles as it holds them (4 rows per
-        // lane); those of slices 2kk and 2kk+1, transposed by an MFMA against the identity,
-        // form the B fragment of columns 32kk.. (done at the point of use below).
-        typename M::frag bs[NKV], bd[NKV];
-        s4i dsr[NKV][2];
-#pragma unroll
-        for (int kk = 0; kk < NKV; ++kk) {
-          bs[kk] = frag_ld<T>(Sin, V, 16 * kt, kk * M::KS, lane);
-          if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-              dsr[kk][b] = *reinterpret_cast<const s4i*>(dSo + ScanFrag<K, V, C>::seed(2 * kk + b, kt, KT, lane));
-          } else {
-            bd[kk] = frag_ld<T>(dSo, V, 16 * kt, kk * M::KS, lane);
-          }
-        }
         f32x4 aq[RT], akd[RT], ai[RT], ar[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) aq[rt] = akd[rt] = ai[rt] = ar[rt] = zero4();
@@ -648,25 +699,25 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
           if constexpr (sizeof(T) == 2) {
-            const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsr[kk][0], ident4, zero4(), 0, 0, 0);
-            const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsr[kk][1], ident4, zero4(), 0, 0, 0);
+            const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsr[ci][kk][0], ident4, zero4(), 0, 0, 0);
+            const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsr[ci][kk][1], ident4, zero4(), 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              bd[kk][i] = (bf16)d0[i];
-              bd[kk][4 + i] = (bf16)d1[i];
+              bd[ci][kk][i] = (bf16)d0[i];
+              bd[ci][kk][4 + i] = (bf16)d1[i];
             }
           }
           if constexpr (M::PER == 8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) rsum += (float)bs[kk][i] * (float)bd[kk][i];
+            for (int i = 0; i < 8; ++i) rsum += (float)bs[ci][kk][i] * (float)bd[ci][kk][i];
           } else {
-            rsum += bs[kk] * bd[kk];
+            rsum += bs[ci][kk] * bd[ci][kk];
           }
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
-            aq[rt] = M::mma(frag_ld<T>(DoR, LDV, 16 * rt, kk * M::KS, lane), bs[kk], aq[rt]);
-            akd[rt] = M::mma(frag_ld<T>(Ndv, LDV, 16 * rt, kk * M::KS, lane), bs[kk], akd[rt]);
-            ar[rt] = M::mma(frag_ld<T>(U, LDV, 16 * rt, kk * M::KS, lane), bd[kk], ar[rt]);
+            aq[rt] = M::mma(frag_ld<T>(DoR, LDV, 16 * rt, kk * M::KS, lane), bs[ci][kk], aq[rt]);
+            akd[rt] = M::mma(frag_ld<T>(Ndv, LDV, 16 * rt, kk * M::KS, lane), bs[ci][kk], akd[rt]);
+            ar[rt] = M::mma(frag_ld<T>(U, LDV, 16 * rt, kk * M::KS, lane), bd[ci][kk], ar[rt]);
           }
         }
         rsum = col_allsum(rsum);

@@ -11,6 +11,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace kda {
@@ -199,6 +200,64 @@ __device__ __forceinline__ void col_load(float (&x)[RT][4], const T* __restrict_
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) x[rt][j] = 16 * rt + 4 * grp + j < len ? to_f(raw[rt][j]) : 0.f;
+}
+
+// Same result as col_load for the 16 columns col0 .. col0+15 (this lane: col0 + lane%16),
+// from one row-vector load per 16 x 16 tile: lane (n, grp) reads row row0 + 16rt + n, columns
+// col0 + 4grp .. +3 (8 bytes of bf16 or 16 of fp32, so ld and col0 must keep those
+// aligned), and MFMAs turn the tile into the column-owner layout: a bf16 16x16x16 against
+// the identity, or four fp32 16x16x4 against 0/1 selectors that each place the columns
+// c with c % 4 == j. Both are exact (one nonzero product per output). Rows are clamped to
+// len - 1 (len >= 1) and read as zero from len on. load() only issues the loads, so that a
+// caller can issue all of its loads before the first get() waits. Whole-wave only.
+template <class T, int RT>
+struct ColTile {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef typename std::conditional<sizeof(T) == 2, s4, f32x4>::type raw_t;
+  raw_t raw[RT];
+  __device__ __forceinline__ void load(const T* __restrict__ base, int ld, int col0, int lane, int len, int row0 = 0) {
+    const int n = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+      raw[rt] = *reinterpret_cast<const raw_t*>(base + min(row0 + 16 * rt + n, len - 1) * ld + col0 + 4 * grp);
+  }
+  __device__ __forceinline__ void get(float (&x)[RT][4], int lane, int len, int row0 = 0) const {
+    const int n = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 d;
+      if constexpr (sizeof(T) == 2) {
+        s4 id;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) id[j] = (4 * grp + j == n) ? (short)0x3f80 : (short)0;
+        d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(raw[rt], id, zero4(), 0, 0, 0);
+      } else {
+        d = zero4();
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          d = __builtin_amdgcn_mfma_f32_16x16x4f32(raw[rt][j], n == 4 * grp + j ? 1.f : 0.f, d, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[rt][j] = row0 + 16 * rt + 4 * grp + j < len ? d[j] : 0.f;
+    }
+  }
+};
+
+// The inverse move for bf16 tiles: the values this lane holds in the column-owner layout
+// (column lane%16, rows 4(lane/16) .. +3), rounded to bf16, fed as the A operand of an MFMA
+// against the identity come out in the row layout: this lane then holds row lane%16,
+// columns 4(lane/16) .. +3 (exact, as bf16 values). Whole-wave only.
+__device__ __forceinline__ f32x4 to_rows_bf16(float x0, float x1, float x2, float x3, int lane) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const int n = lane & 15, grp = lane >> 4;
+  const bf16 b[4] = {(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
+  s4 a, id;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = __builtin_bit_cast(short, b[j]);
+    id[j] = (4 * grp + j == n) ? (short)0x3f80 : (short)0;
+  }
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, id, zero4(), 0, 0, 0);
 }
 
 // Inclusive prefix sum over rows of one column: x[rt][j] holds row 16*rt + 4*grp + j.
