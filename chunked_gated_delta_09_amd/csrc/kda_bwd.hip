@@ -559,9 +559,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         INVt, LDC, 1 << 30, VcT, LDC, [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
         [&](int, int mt, int nt0, f32x4(&acc)[BN1]) {
 #pragma unroll
-          for (int jb = 0; jb < BN1; ++jb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) U[(16 * mt + 4 * grp + j) * LDV + 16 * (nt0 + jb) + n] = from_f<T>(acc[jb][j]);
+          for (int jb = 0; jb < BN1; ++jb) store_rows<T>(U, LDV, 16 * mt, 16 * (nt0 + jb), acc[jb], lane, 1 << 30);
         }, wave, lane);
     __syncthreads();
 
@@ -594,15 +592,17 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
           float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int jb = 0; jb < BN1; ++jb) {
-            const int col = 16 * (nt0 + jb) + n;
+            f32x4 ndv, dvb;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int row = 16 * mt + 4 * grp + j;
               const float dvc = acc[jb][j];
-              Ndv[row * LDV + col] = from_f<T>(-dvc);
-              if (row < len) dvc_out[row * vs + col] = from_f<T>(betas[row] * dvc);
+              ndv[j] = -dvc;
+              dvb[j] = betas[row] * dvc;
               part[j] += dvc * to_f(vraw[it][jb][j]);
             }
+            store_rows<T>(Ndv, LDV, 16 * mt, 16 * (nt0 + jb), ndv, lane, 1 << 30);
+            store_rows<T>(dvc_out, vs, 16 * mt, 16 * (nt0 + jb), dvb, lane, len);
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -645,21 +645,21 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
             m4[j] = col <= row ? acc[0][j] : 0.f;
-            DMqk[row * LDC + col] = from_f<T>(m4[j]);
           }
+          store_rows<T>(DMqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
           st4(DMqkT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, m4);
         }, wave, lane);
     block_gemm<T, RT, RT, 1, NW, V>(
         Ndv, LDV, 1 << 30, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
         [&](int it, int mt, int nt0, f32x4(&acc)[1]) {
-          f32x4 b4;
+          f32x4 b4, l4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
-            const float l = col < row ? acc[0][j] : 0.f;
-            DL[row * LDC + col] = from_f<T>(l);
-            b4[j] = betas[row] * l;
+            l4[j] = col < row ? acc[0][j] : 0.f;
+            b4[j] = betas[row] * l4[j];
           }
+          store_rows<T>(DL, LDC, 16 * mt, 16 * nt0, l4, lane, 1 << 30);
           st4(BDLT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, b4);
         }, wave, lane);
     __syncthreads();
@@ -727,6 +727,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           float dbz[4];
+          f32x4 dq4, dk4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * rt + 4 * grp + j;
@@ -734,16 +735,19 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
             const float eG = __expf(G), emG = __expf(-G), erG = __expf(g_last - G);
             const float dq_e = s.scale * eG * aq[rt][j];
             const float dk_d = eG * betas[row] * akd[rt][j], dk_i = emG * ai[rt][j], dk_r = erG * ar[rt][j];
+            dq4[j] = dq_e;
+            dk4[j] = dk_d + dk_i + dk_r;
             if constexpr (GVA) {
               dqa[ci][rt][j] += dq_e;
-              dka[ci][rt][j] += dk_d + dk_i + dk_r;
-            } else if (row < len) {
-              dqc[row * qs + col] = from_f<T>(dq_e);
-              dkc[row * qs + col] = from_f<T>(dk_d + dk_i + dk_r);
+              dka[ci][rt][j] += dk4[j];
             }
             dG[rt][j] = qv[ci][rt][j] * dq_e + kv[ci][rt][j] * (dk_d - dk_i - dk_r);
             krd += kv[ci][rt][j] * dk_r;
             dbz[j] = kv[ci][rt][j] * eG * akd[rt][j];  // dbeta part 2: rowsum(kd o akd)
+          }
+          if constexpr (!GVA) {
+            store_rows<T>(dqc, qs, 16 * rt, 16 * kt, dq4, lane, len);
+            store_rows<T>(dkc, qs, 16 * rt, 16 * kt, dk4, lane, len);
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -819,17 +823,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
   for (int ci = 0; ci < NACC; ++ci) {
     const int kt = wave + ci * NW;
     if (kt < KT) {
-      const int col = 16 * kt + n;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 16 * rt + 4 * grp + j;
-          if (row < len) {
-            dqc[row * qs + col] = from_f<T>(dqa[ci][rt][j]);
-            dkc[row * qs + col] = from_f<T>(dka[ci][rt][j]);
-          }
-        }
+      for (int rt = 0; rt < RT; ++rt) {
+        store_rows<T>(dqc, qs, 16 * rt, 16 * kt, f32x4{dqa[ci][rt][0], dqa[ci][rt][1], dqa[ci][rt][2], dqa[ci][rt][3]}, lane, len);
+        store_rows<T>(dkc, qs, 16 * rt, 16 * kt, f32x4{dka[ci][rt][0], dka[ci][rt][1], dka[ci][rt][2], dka[ci][rt][3]}, lane, len);
+      }
     }
   }
   KDA_TS(2, 9);

@@ -260,6 +260,23 @@ __device__ __forceinline__ f32x4 to_rows_bf16(float x0, float x1, float x2, floa
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, id, zero4(), 0, 0, 0);
 }
 
+// Writes the 16 x 16 tile this wave holds in the column-owner layout (x[j]: row
+// r0 + 4(lane/16) + j, column c0 + lane%16) into a row-major array with row stride ld,
+// skipping rows >= rmax. bf16: transposed by to_rows_bf16, one 8-byte piece per lane
+// (row r0 + lane%16, columns c0 + 4(lane/16) ..); fp32: element by element. Whole-wave.
+template <class T>
+__device__ __forceinline__ void store_rows(T* __restrict__ base, int ld, int r0, int c0, f32x4 x, int lane, int rmax) {
+  const int n = lane & 15, grp = lane >> 4;
+  if constexpr (sizeof(T) == 2) {
+    const f32x4 r = to_rows_bf16(x[0], x[1], x[2], x[3], lane);
+    if (r0 + n < rmax) st4(base + (r0 + n) * ld + c0 + 4 * grp, r);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (r0 + 4 * grp + j < rmax) base[(r0 + 4 * grp + j) * ld + c0 + n] = x[j];
+  }
+}
+
 // Inclusive prefix sum over rows of one column: x[rt][j] holds row 16*rt + 4*grp + j.
 template <int RT>
 __device__ __forceinline__ void col_prefix(float (&x)[RT][4], int lane) {
