@@ -118,8 +118,7 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
     const int kt = wave + ci * NW;
     if (kt < KT) {
       const int col = 16 * kt + n;
-      col_prefix<RT>(G[ci], lane);
-      const float gam = __shfl(G[ci][RT - 1][3], n + 48, 64);
+      const float gam = col_prefix<RT>(G[ci], lane);  // the column total is gam
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         f32x4 bk;
@@ -438,8 +437,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       gam[ci] = 0.f;
       if (kt < KT) {
         const int col = 16 * kt + n;
-        col_prefix<RT>(Gr[ci], lane);
-        gam[ci] = __shfl(Gr[ci][RT - 1][3], n + 48, 64);
+        gam[ci] = col_prefix<RT>(Gr[ci], lane);  // the column total is gam
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           f32x4 q4, kd4, ki4;

@@ -277,75 +277,64 @@ __device__ __forceinline__ void store_rows(T* __restrict__ base, int ld, int r0,
   }
 }
 
+// Sums across the 4 lane groups of a column (lanes n, n+16, n+32, n+48) are one fp32
+// 16x16x4 MFMA: this lane's value is B[grp][n], and the constant A (lane n_a, grp_a
+// supplies A[n_a][grp_a]) picks which groups each output row adds, so output element j
+// of this lane is sum over kappa of A[4grp + j][kappa] * value(n, kappa). Exact in fp32.
+// Whole-wave only.
+__device__ __forceinline__ f32x4 col_mix(float a, float v) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, v, zero4(), 0, 0, 0);
+}
+
 // Inclusive prefix sum over rows of one column: x[rt][j] holds row 16*rt + 4*grp + j.
+// Returns the column total.
 template <int RT>
-__device__ __forceinline__ void col_prefix(float (&x)[RT][4], int lane) {
-  float tot[RT];
+__device__ __forceinline__ float col_prefix(float (&x)[RT][4], int lane) {
+  const int n = lane & 15, grp = lane >> 4;
+  // rows 4g+j, j < 3: groups before g; rows 4g+3: every group
+  const float a = (n & 3) == 3 ? 1.f : (grp < (n >> 2) ? 1.f : 0.f);
+  float carry = 0.f;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     x[rt][1] += x[rt][0];
     x[rt][2] += x[rt][1];
     x[rt][3] += x[rt][2];
-    tot[rt] = x[rt][3];
+    const f32x4 d = col_mix(a, x[rt][3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[rt][j] += carry + d[0];
+    carry += d[3];
   }
-  const int n = lane & 15, grp = lane >> 4;
-  float carry = 0.f;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    float before = carry, all = 0.f;
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      const float b = __shfl(tot[rt], n + 16 * gg, 64);
-      if (gg < grp) before += b;
-      all += b;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[rt][j] += before;
-    carry += all;
-  }
+  return carry;
 }
 
 // Inclusive suffix (reverse) sum over rows of one column.
 template <int RT>
 __device__ __forceinline__ void col_suffix(float (&x)[RT][4], int lane) {
-  float tot[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    x[rt][2] += x[rt][3];
-    x[rt][1] += x[rt][2];
-    x[rt][0] += x[rt][1];
-    tot[rt] = x[rt][0];
-  }
   const int n = lane & 15, grp = lane >> 4;
+  const float a = (n & 3) == 3 ? 1.f : (grp > (n >> 2) ? 1.f : 0.f);
   float carry = 0.f;
 #pragma unroll
   for (int rt = RT - 1; rt >= 0; --rt) {
-    float after = carry, all = 0.f;
+    x[rt][2] += x[rt][3];
+    x[rt][1] += x[rt][2];
+    x[rt][0] += x[rt][1];
+    const f32x4 d = col_mix(a, x[rt][0]);
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      const float b = __shfl(tot[rt], n + 16 * gg, 64);
-      if (gg > grp) after += b;
-      all += b;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[rt][j] += after;
-    carry += all;
+    for (int j = 0; j < 4; ++j) x[rt][j] += carry + d[0];
+    carry += d[3];
   }
 }
 
 // Sum over the 4 lanes that share a column (same l % 16).
-__device__ __forceinline__ float col_allsum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
-}
+__device__ __forceinline__ float col_allsum(float v) { return col_mix(1.f, v)[0]; }
 
-// Sum over the 16 lanes of one lane group (same rows, the 16 columns of a tile).
+// Sum over the 16 lanes of one lane group (same rows, the 16 columns of a tile): DPP
+// rotations within the 16-lane row by 8, 4, 2 and 1.
 __device__ __forceinline__ float row_allsum16(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));
   return v;
 }
 

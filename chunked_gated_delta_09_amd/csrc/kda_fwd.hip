@@ -99,8 +99,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(Shape s, const T* __restr
         const int row = 16 * rt + 4 * grp + j;
         G[rt][j] = row < len ? gc[row * gs + col] : 0.f;
       }
-    col_prefix<RT>(G, lane);
-    const float gam = __shfl(G[RT - 1][3], n + 48, 64);
+    const float gam = col_prefix<RT>(G, lane);  // the column total is gam
     T* __restrict__ krT = reinterpret_cast<T*>(ws.krT) + ch * (sizeof(T) == 2 ? ScanFrag<K, V, C>::P2_ELEMS : K * C);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
