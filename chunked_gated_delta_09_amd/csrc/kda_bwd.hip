@@ -362,25 +362,54 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       tq[ci].load(qc, qs, 16 * kt, lane, len);
       tk[ci].load(kc, qs, 16 * kt, lane, len);
     }
-    // S_in as 16-byte row pieces: piece i of this thread is row (pid % K), columns
-    // VEC*(pid / K) .. +VEC-1, so the lanes of a wave cover consecutive rows.
+    // S_in, INV and dO as 16-byte row pieces. bf16 (BLK): piece i of this lane is in 16 x 32
+    // block b = wave + i*NW of the matrix (blocks down the rows first), row 16(b % row
+    // tiles) + n, columns 32(b / row tiles) + 8grp .. +7, so each block can be written
+    // transposed into LDS by store_T_block. Otherwise piece i of thread tid covers elements
+    // VEC*pid .. of a row, pid = tid + i*NTH (S_in: lanes on consecutive rows).
+    constexpr bool BLK = sizeof(T) == 2 && C % 32 == 0 && V % 32 == 0 && K % 16 == 0;
+    constexpr int NBS = KT * (V / 32), NBI = RT * (C / 32), NBD = RT * (V / 32);
+    auto blk_rc = [&](int b, int rtiles, int& r, int& c) {
+      r = 16 * (b % rtiles) + n;
+      c = 32 * (b / rtiles) + 8 * grp;
+    };
     constexpr int NSV = (K * V / VEC + NTH - 1) / NTH;
     vecT sv[NSV];
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
-      const int pid = min(tid + i * NTH, K * V / VEC - 1);
-      sv[i] = *reinterpret_cast<const vecT*>(Sin + (pid % K) * V + (pid / K) * VEC);
+      if constexpr (BLK) {
+        int r, c;
+        blk_rc(min(wave + i * NW, NBS - 1), KT, r, c);
+        sv[i] = *reinterpret_cast<const vecT*>(Sin + r * V + c);
+      } else {
+        const int pid = min(tid + i * NTH, K * V / VEC - 1);
+        sv[i] = *reinterpret_cast<const vecT*>(Sin + (pid % K) * V + (pid / K) * VEC);
+      }
     }
     constexpr int NIV = (C * C / VEC + NTH - 1) / NTH;
     vecT iv[NIV];
 #pragma unroll
-    for (int i = 0; i < NIV; ++i) iv[i] = *reinterpret_cast<const vecT*>(invc + min(tid + i * NTH, C * C / VEC - 1) * VEC);
+    for (int i = 0; i < NIV; ++i) {
+      if constexpr (BLK) {
+        int r, c;
+        blk_rc(min(wave + i * NW, NBI - 1), RT, r, c);
+        iv[i] = *reinterpret_cast<const vecT*>(invc + r * C + c);
+      } else {
+        iv[i] = *reinterpret_cast<const vecT*>(invc + min(tid + i * NTH, C * C / VEC - 1) * VEC);
+      }
+    }
     vecT dov[NDV];
 #pragma unroll
     for (int i = 0; i < NDV; ++i) {
-      const int vi = min(tid + i * NTH, NVEC - 1);
-      const int row = vi / (V / VEC), c8 = vi % (V / VEC);
-      dov[i] = *reinterpret_cast<const vecT*>(dOc + min(row, len - 1) * vs + c8 * VEC);
+      int row, c;
+      if constexpr (BLK) {
+        blk_rc(min(wave + i * NW, NBD - 1), RT, row, c);
+      } else {
+        const int vi = min(tid + i * NTH, NVEC - 1);
+        row = vi / (V / VEC);
+        c = (vi % (V / VEC)) * VEC;
+      }
+      dov[i] = *reinterpret_cast<const vecT*>(dOc + min(row, len - 1) * vs + c);
       if (row >= len) dov[i] = vecT{};
     }
     // v at the places of the C x V accumulator tiles this wave owns in the block walk of
@@ -468,11 +497,16 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     }
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
-      const int pid = tid + i * NTH;
-      if (pid < K * V / VEC) {
-        const int row = pid % K, c0 = (pid / K) * VEC;
+      if constexpr (BLK) {
+        const int b = wave + i * NW;
+        if (b < NBS) store_T_block(SinT, LDK, 16 * (b % KT), 32 * (b / KT), sv[i], lane);
+      } else {
+        const int pid = tid + i * NTH;
+        if (pid < K * V / VEC) {
+          const int row = pid % K, c0 = (pid / K) * VEC;
 #pragma unroll
-        for (int t = 0; t < VEC; ++t) SinT[(c0 + t) * LDK + row] = sv[i][t];
+          for (int t = 0; t < VEC; ++t) SinT[(c0 + t) * LDK + row] = sv[i][t];
+        }
       }
     }
     __syncthreads();
@@ -480,15 +514,28 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     // INV and INV^T (read first by U = INV vcorr, after the next barrier)
 #pragma unroll
     for (int i = 0; i < NIV; ++i) {
-      const int pid = tid + i * NTH;
-      if (pid < C * C / VEC) {
-        const int r = (pid * VEC) / C, c0 = (pid * VEC) % C;
+      if constexpr (BLK) {
+        const int b = wave + i * NW;
+        if (b < NBI) {
+          int r, c0;
+          blk_rc(b, RT, r, c0);
+          vecT m;
 #pragma unroll
-        for (int t = 0; t < VEC; ++t) {
-          const int cc = c0 + t;
-          const T val = (r < len && cc < len) ? iv[i][t] : from_f<T>(r == cc ? 1.f : 0.f);
-          INVt[r * LDC + cc] = val;
-          INVTt[cc * LDC + r] = val;
+          for (int t = 0; t < VEC; ++t) m[t] = (r < len && c0 + t < len) ? iv[i][t] : from_f<T>(r == c0 + t ? 1.f : 0.f);
+          *reinterpret_cast<vecT*>(INVt + r * LDC + c0) = m;
+          store_T_block(INVTt, LDC, 16 * (b % RT), 32 * (b / RT), m, lane);
+        }
+      } else {
+        const int pid = tid + i * NTH;
+        if (pid < C * C / VEC) {
+          const int r = (pid * VEC) / C, c0 = (pid * VEC) % C;
+#pragma unroll
+          for (int t = 0; t < VEC; ++t) {
+            const int cc = c0 + t;
+            const T val = (r < len && cc < len) ? iv[i][t] : from_f<T>(r == cc ? 1.f : 0.f);
+            INVt[r * LDC + cc] = val;
+            INVTt[cc * LDC + r] = val;
+          }
         }
       }
     }
@@ -545,11 +592,16 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     }
 #pragma unroll
     for (int i = 0; i < NDV; ++i) {
-      const int vi = tid + i * NTH;
-      if (vi < NVEC) {
-        const int row = vi / (V / VEC), c8 = vi % (V / VEC);
+      if constexpr (BLK) {
+        const int b = wave + i * NW;
+        if (b < NBD) store_T_block(DoT, LDC, 16 * (b % RT), 32 * (b / RT), dov[i], lane);
+      } else {
+        const int vi = tid + i * NTH;
+        if (vi < NVEC) {
+          const int row = vi / (V / VEC), c8 = vi % (V / VEC);
 #pragma unroll
-        for (int t = 0; t < VEC; ++t) DoT[(c8 * VEC + t) * LDC + row] = dov[i][t];
+          for (int t = 0; t < VEC; ++t) DoT[(c8 * VEC + t) * LDC + row] = dov[i][t];
+        }
       }
     }
     // ---- U = INV vcorr (row-major)
@@ -578,10 +630,19 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     // ---- dO row-major (into the dead dO^T slot); dvc = INV^T dU -> -dvc, dv, dbeta part 1
 #pragma unroll
     for (int i = 0; i < NDV; ++i) {
-      const int vi = tid + i * NTH;
-      if (vi < NVEC) {
-        const int row = vi / (V / VEC), c8 = vi % (V / VEC);
-        *reinterpret_cast<vecT*>(DoR + row * LDV + c8 * VEC) = dov[i];
+      if constexpr (BLK) {
+        const int b = wave + i * NW;
+        if (b < NBD) {
+          int r, c;
+          blk_rc(b, RT, r, c);
+          *reinterpret_cast<vecT*>(DoR + r * LDV + c) = dov[i];
+        }
+      } else {
+        const int vi = tid + i * NTH;
+        if (vi < NVEC) {
+          const int row = vi / (V / VEC), c8 = vi % (V / VEC);
+          *reinterpret_cast<vecT*>(DoR + row * LDV + c8 * VEC) = dov[i];
+        }
       }
     }
     block_gemm<T, RT, VT, BN1, NW, C>(

@@ -250,13 +250,10 @@ struct ColTile {
 __device__ __forceinline__ f32x4 to_rows_bf16(float x0, float x1, float x2, float x3, int lane) {
   typedef short s4 __attribute__((ext_vector_type(4)));
   const int n = lane & 15, grp = lane >> 4;
-  const bf16 b[4] = {(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
-  s4 a, id;
+  const s4 a = __builtin_bit_cast(s4, bf16x4{(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3});
+  s4 id;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    a[j] = __builtin_bit_cast(short, b[j]);
-    id[j] = (4 * grp + j == n) ? (short)0x3f80 : (short)0;
-  }
+  for (int j = 0; j < 4; ++j) id[j] = (4 * grp + j == n) ? (short)0x3f80 : (short)0;
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, id, zero4(), 0, 0, 0);
 }
 
@@ -284,6 +281,29 @@ __device__ __forceinline__ void store_rows(T* __restrict__ base, int ld, int r0,
 // Whole-wave only.
 __device__ __forceinline__ f32x4 col_mix(float a, float v) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, v, zero4(), 0, 0, 0);
+}
+
+// A 16 x 32 block of a row-major bf16 matrix M held as one 16-byte piece per lane (row
+// r0 + lane%16, columns c0 + 8(lane/16) .. +7) is written transposed into dst:
+// M[r][c] goes to dst[c * ldd + r]. Each half of the pieces is turned around by an MFMA
+// against the identity, so every lane writes two 8-byte pieces (4 consecutive rows of one
+// column). Whole-wave only.
+__device__ __forceinline__ void store_T_block(bf16* __restrict__ dst, int ldd, int r0, int c0, bf16x8 piece, int lane) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef short s8 __attribute__((ext_vector_type(8)));
+  const int n = lane & 15, grp = lane >> 4;
+  s4 id;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) id[j] = (4 * grp + j == n) ? (short)0x3f80 : (short)0;
+  // whole-vector bit cast (element-wise casts of __bf16 vector elements are not relied on)
+  const s8 ps = __builtin_bit_cast(s8, piece);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const s4 a = {ps[4 * h], ps[4 * h + 1], ps[4 * h + 2], ps[4 * h + 3]};
+    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, id, zero4(), 0, 0, 0);
+    // this lane: rows r0 + 4grp .. +3 of column c0 + 8(n/4) + 4h + n%4
+    st4(dst + (c0 + 8 * (n >> 2) + 4 * h + (n & 3)) * ldd + r0 + 4 * grp, d);
+  }
 }
 
 // Inclusive prefix sum over rows of one column: x[rt][j] holds row 16*rt + 4*grp + j.
