@@ -103,12 +103,11 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
     const int vt = wave + cv * NW;
     if (vt < VT) col_load<T, RT>(dov[cv], dOc, vs, 16 * vt + n, grp, len);
   }
-  T invr[NI];
+  typedef T vecT __attribute__((ext_vector_type(16 / sizeof(T))));
+  constexpr int VEC = 16 / (int)sizeof(T), NIV = (C * C / VEC + NTH - 1) / NTH;
+  vecT iv[NIV];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int idx = tid + i * NTH;
-    invr[i] = idx < C * C ? invc[idx] : (T)0.0f;
-  }
+  for (int i = 0; i < NIV; ++i) iv[i] = *reinterpret_cast<const vecT*>(invc + min(tid + i * NTH, C * C / VEC - 1) * VEC);
   if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
   __syncthreads();
 
@@ -121,20 +120,24 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
       const float gam = col_prefix<RT>(G[ci], lane);  // the column total is gam
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        f32x4 bk;
+        f32x4 bk, qd4, ki4, kr4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * rt + 4 * grp + j;
           const float e = __expf(G[ci][rt][j]);
-          Qd[row * LDK + col] = from_f<T>(s.scale * qv[ci][rt][j] * e);
-          Ki[row * LDK + col] = from_f<T>(kv[ci][rt][j] * __expf(-G[ci][rt][j]));
+          qd4[j] = s.scale * qv[ci][rt][j] * e;
+          ki4[j] = kv[ci][rt][j] * __expf(-G[ci][rt][j]);
           bk[j] = betas[row] * kv[ci][rt][j] * e;
-          const T krv = from_f<T>(kv[ci][rt][j] * __expf(gam - G[ci][rt][j]));
-          if constexpr (sizeof(T) == 2) {
-            krg[ScanFrag<K, V, C>::p1(row, col)] = krv;
-          } else {
-            krg[row * K + col] = krv;
-          }
+          kr4[j] = kv[ci][rt][j] * __expf(gam - G[ci][rt][j]);
+        }
+        store_rows<T>(Qd, LDK, 16 * rt, 16 * kt, qd4, lane, 1 << 30);
+        store_rows<T>(Ki, LDK, 16 * rt, 16 * kt, ki4, lane, 1 << 30);
+        if constexpr (sizeof(T) == 2) {
+          // row layout (this lane: row 16rt + n, columns 16kt + 4grp ..): one 8-byte piece
+          st4(krg + ScanFrag<K, V, C>::p1(16 * rt + n, 16 * kt + 4 * grp), to_rows_bf16(kr4[0], kr4[1], kr4[2], kr4[3], lane));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) krg[(16 * rt + 4 * grp + j) * K + col] = kr4[j];
         }
         st4(BKdT + col * LDC + 16 * rt + 4 * grp, bk);
       }
@@ -152,11 +155,14 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
     }
   }
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int idx = tid + i * NTH;
-    if (idx < C * C) {
-      const int r = idx / C, cc = idx % C;
-      INVt[r * LDC + cc] = (r < len && cc < len) ? invr[i] : from_f<T>(r == cc ? 1.f : 0.f);
+  for (int i = 0; i < NIV; ++i) {
+    const int pid = tid + i * NTH;
+    if (pid < C * C / VEC) {
+      const int r = (pid * VEC) / C, c0 = (pid * VEC) % C;
+      vecT m;
+#pragma unroll
+      for (int t = 0; t < VEC; ++t) m[t] = (r < len && c0 + t < len) ? iv[i][t] : from_f<T>(r == c0 + t ? 1.f : 0.f);
+      *reinterpret_cast<vecT*>(INVt + r * LDC + c0) = m;
     }
   }
   __syncthreads();
@@ -166,11 +172,13 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
   block_gemm<T, RT, RT, 1, NW, K>(
       Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
       [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+        f32x4 m4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
-          Mqk[row * LDC + col] = from_f<T>(col <= row ? acc[0][j] : 0.f);
+          m4[j] = col <= row ? acc[0][j] : 0.f;
         }
+        store_rows<T>(Mqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
       }, wave, lane);
   // w = INV diag(beta) kd: kept transposed in LDS, stored negated and transposed for the scan.
   T* __restrict__ nwT = reinterpret_cast<T*>(ws.nwT) + ch * (sizeof(T) == 2 ? ScanFrag<K, V, C>::P2_ELEMS : K * C);
