@@ -30,6 +30,12 @@ extern "C" __attribute__((visibility("default"))) int kda_phase_ts_read(void* ho
 }
 #endif
 
+// LDS plan of the bwd prep kernel, small enough for two workgroups per CU. Later buffers
+// overlay earlier ones that a barrier has retired:
+//   Qd, Ki (phases 0-2)            -> dO^T (phase 3)
+//   beta kd^T (phases 0-1a)        -> Q'^T (phases 2-3)
+//   INV (phases 0-1a)              -> Mqk (phases 1b-2)
+//   W^T (phases 1a-2)
 template <class T, int K, int V, int C>
 struct BwdPrepLds {
   static constexpr int NW = 8;
@@ -37,19 +43,21 @@ struct BwdPrepLds {
   static constexpr int LDK = K + P, LDC = C + P;
   static constexpr size_t oQd = 0;
   static constexpr size_t oKi = oQd + sizeof(T) * C * LDK;
+  static constexpr size_t oDoT = 0;
   static constexpr size_t oBKdT = oKi + sizeof(T) * C * LDK;
-  static constexpr size_t oDoT = oBKdT + sizeof(T) * K * LDC;
-  static constexpr size_t oINV = oDoT + sizeof(T) * V * LDC;
-  static constexpr size_t oMqk = oINV + sizeof(T) * C * LDC;
-  static constexpr size_t oWT = oMqk + sizeof(T) * C * LDC;
-  static constexpr size_t oQpT = oWT + sizeof(T) * K * LDC;
-  static constexpr size_t oBeta = oQpT + sizeof(T) * K * LDC;
+  static constexpr size_t oQpT = oBKdT;
+  static constexpr size_t oINV = oBKdT + sizeof(T) * K * LDC;
+  static constexpr size_t oMqk = oINV;
+  static constexpr size_t oWT = oINV + sizeof(T) * C * LDC;
+  static constexpr size_t oBeta = oWT + sizeof(T) * K * LDC;
   static constexpr size_t total = oBeta + sizeof(float) * C;
+  static_assert(sizeof(T) * V * LDC <= oBKdT, "dO^T overlays Qd and Ki");
 };
 
-// One workgroup per (chunk, value head).
+// One workgroup per (chunk, value head); two fit on a CU (LDS plan above, at most 128
+// VGPRs), so one's loads overlap the other's products.
 template <class T, int K, int V, int C>
-__global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
+__global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
                                                         const float* __restrict__ gp, const float* __restrict__ bp,
                                                         const T* __restrict__ invp, const T* __restrict__ dOp,
                                                         BwdWs ws) {
@@ -145,16 +153,6 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
     }
   }
 #pragma unroll
-  for (int cv = 0; cv < NCV; ++cv) {
-    const int vt = wave + cv * NW;
-    if (vt < VT) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        st4(DoT + (16 * vt + n) * LDC + 16 * rt + 4 * grp,
-            f32x4{dov[cv][rt][0], dov[cv][rt][1], dov[cv][rt][2], dov[cv][rt][3]});
-    }
-  }
-#pragma unroll
   for (int i = 0; i < NIV; ++i) {
     const int pid = tid + i * NTH;
     if (pid < C * C / VEC) {
@@ -168,18 +166,6 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
   __syncthreads();
 
   KDA_TS(0, 1);
-  // Mqk = tril(qd ki^T), row-major.
-  block_gemm<T, RT, RT, 1, NW, K>(
-      Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
-      [&](int, int mt, int nt0, f32x4(&acc)[1]) {
-        f32x4 m4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
-          m4[j] = col <= row ? acc[0][j] : 0.f;
-        }
-        store_rows<T>(Mqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
-      }, wave, lane);
   // w = INV diag(beta) kd: kept transposed in LDS, stored negated and transposed for the scan.
   T* __restrict__ nwT = reinterpret_cast<T*>(ws.nwT) + ch * (sizeof(T) == 2 ? ScanFrag<K, V, C>::P2_ELEMS : K * C);
   constexpr int BNK = KT % 2 == 0 ? 2 : 1;
@@ -197,6 +183,19 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
           }
         }
       }, wave, lane);
+  __syncthreads();  // INV and beta kd^T retired
+  // Mqk = tril(qd ki^T), row-major.
+  block_gemm<T, RT, RT, 1, NW, K>(
+      Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
+      [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+        f32x4 m4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
+          m4[j] = col <= row ? acc[0][j] : 0.f;
+        }
+        store_rows<T>(Mqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
+      }, wave, lane);
   __syncthreads();
   KDA_TS(0, 2);
   // Q' = qd - Mqk w, transposed.
@@ -212,6 +211,18 @@ __global__ __launch_bounds__(512) void bwd_prep_kernel(Shape s, const T* __restr
           st4(QpT + col * LDC + 16 * mt + 4 * grp, qp4);
         }
       }, wave, lane);
+  __syncthreads();  // Qd, Ki, Mqk, W^T retired
+  // dO^T over Qd and Ki
+#pragma unroll
+  for (int cv = 0; cv < NCV; ++cv) {
+    const int vt = wave + cv * NW;
+    if (vt < VT) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        st4(DoT + (16 * vt + n) * LDC + 16 * rt + 4 * grp,
+            f32x4{dov[cv][rt][0], dov[cv][rt][1], dov[cv][rt][2], dov[cv][rt][3]});
+    }
+  }
   __syncthreads();
   KDA_TS(0, 3);
   // W = Q'^T dO, stored transposed [V][K].
