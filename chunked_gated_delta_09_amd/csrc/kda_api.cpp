@@ -151,6 +151,8 @@ kda::Shape make_shape(const kda_dims* d, const Plan& p, void* ws, size_t choff_o
   s.scale = d->scale;
   s.cu = p.varlen ? d->cu_seqlens_dev : nullptr;
   s.choff = p.varlen ? reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + choff_off) : nullptr;
+  s.hv0 = 0;
+  s.nhv = d->HV;
   return s;
 }
 

@@ -15,6 +15,7 @@ struct Shape {
   float scale;
   const int32_t* cu;     // device cu_seqlens, or nullptr when dense
   const int32_t* choff;  // device first-chunk table [N+1], or nullptr when dense
+  int hv0, nhv;          // value heads of this launch: hv0 .. hv0 + nhv - 1 (a multiple of HV / H)
 };
 
 // Per-chunk workspace tensors of the forward (all [NT, HV, ...]).

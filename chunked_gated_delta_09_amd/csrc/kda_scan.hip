@@ -29,7 +29,7 @@ __global__ __launch_bounds__(64) void scan_kernel(Shape s, const T* __restrict__
                                                    float* __restrict__ Xfin) {
   typedef Mma<T> M;
   constexpr int KT = K / 16, CT = C / 16;
-  const int vt = blockIdx.x, h = blockIdx.y, nseq = blockIdx.z;
+  const int vt = blockIdx.x, h = s.hv0 + blockIdx.y, nseq = blockIdx.z;
   const int lane = threadIdx.x, n = lane & 15, grp = lane >> 4;
   const int vcol = 16 * vt + n;
   int c0, nc;
@@ -186,8 +186,8 @@ __global__ __launch_bounds__(128) void scan_bf16_kernel(Shape s, const bf16* __r
   const int xcd = wid % 8, r = wid / 8;
   const int pair = (r / VT) * 8 + xcd;  // (sequence, head) index
   const int vt = r % VT;
-  if (pair >= s.N * s.HV) return;
-  const int h = pair % s.HV, nseq = pair / s.HV;
+  if (pair >= s.N * s.nhv) return;
+  const int h = s.hv0 + pair % s.nhv, nseq = pair / s.nhv;
   const int lane = threadIdx.x & 63, n = lane & 15, grp = lane >> 4;
   const int vcol = FWD ? 16 * vt + n : ScanCols::col(vt, n);
   int c0, nc;
@@ -397,14 +397,14 @@ static hipError_t scan_t(const Shape& s, const void* P1, const void* P2, const v
                          const float* eg, const void* X0, void* Xout, void* Yout, float* Xfin, hipStream_t st) {
   if (s.N == 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    const int pairs = s.N * s.HV;
+    const int pairs = s.N * s.nhv;
     const int grid = ((pairs + 7) / 8) * 8 * (V / 16);
     hipLaunchKernelGGL((scan_bf16_kernel<K, V, C, FWD>), dim3(grid), dim3(128), 0, st, s,
                        static_cast<const bf16*>(P1), static_cast<const bf16*>(P2), static_cast<const bf16*>(Zi),
                        static_cast<const bf16*>(Wi), eg, static_cast<const bf16*>(X0), static_cast<bf16*>(Xout),
                        static_cast<bf16*>(Yout), Xfin);
   } else {
-    hipLaunchKernelGGL((scan_kernel<T, K, V, C, FWD>), dim3(V / 16, s.HV, s.N), dim3(64), 0, st, s,
+    hipLaunchKernelGGL((scan_kernel<T, K, V, C, FWD>), dim3(V / 16, s.nhv, s.N), dim3(64), 0, st, s,
                        static_cast<const T*>(P1), static_cast<const T*>(P2), static_cast<const T*>(Zi),
                        static_cast<const T*>(Wi), eg, static_cast<const T*>(X0), static_cast<T*>(Xout),
                        static_cast<T*>(Yout), Xfin);
