@@ -30,6 +30,27 @@ PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA, flop/s
 PEAK_F32_FLOPS = 157.3e12    # MI355X dense fp32 MFMA
 
 
+def recorded_traffic(workload_name):
+    """HBM bytes per bwd_grad launch measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE,
+    scaled by a plain copy's readings) as recorded in profiles/bwd_grad_w1_counters.md, or None
+    when that record is for another workload or the kernel's sources have changed since."""
+    import hashlib
+    rec = os.path.join(HERE, "profiles", "bwd_grad_w1_counters.md")
+    if not os.path.exists(rec):
+        return None
+    h = hashlib.sha256()
+    for f in ("kda_bwd.hip", "kda_device.h"):
+        with open(os.path.join(HERE, "chunked_gated_delta_09_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    with open(rec) as fh:
+        for line in fh:
+            if line.startswith("bench-traffic:"):
+                kv = dict(t.split("=", 1) for t in line.split()[1:])
+                if kv.get("workload") == workload_name and kv.get("sources-sha256") == h.hexdigest():
+                    return int(kv["bytes"])
+    return None
+
+
 def algorithmic_bytes(w, inp):
     """Bytes the backward must move at least once: reads of q, k, v, dO, g, beta, the chunk
     states and inverses, dS_final; writes of dq, dk, dv, dg, dbeta, dh0."""
@@ -214,7 +235,7 @@ def main():
         "config": {"workload": w.name, "B": B, "T": T, "H": w.H, "HV": w.HV, "K": w.K, "V": w.V, "C": w.C,
                    "token_heads": th, "cache": "cold (1 GiB flush before each step, outside the timed interval)"},
         "roofline": {"bound": "hbm", "kernel": "bwd_grad", "achieved": achieved, "peak": PEAK_HBM_BYTES / 1e9,
-                     "unit": "GB/s", "frac": achieved / (PEAK_HBM_BYTES / 1e9), "traffic": None,
+                     "unit": "GB/s", "frac": achieved / (PEAK_HBM_BYTES / 1e9), "traffic": recorded_traffic(w.name),
                      "algorithmic_bytes_per_launch": abytes,
                      "launch_ms": grad_ms},
         "call_roofline": {"t_roofline_ms": t_roof * 1e3, "frac": t_roof / (ms * 1e-3),
