@@ -160,7 +160,7 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
       vecT m;
 #pragma unroll
       for (int t = 0; t < VEC; ++t) m[t] = (r < len && c0 + t < len) ? iv[i][t] : from_f<T>(r == c0 + t ? 1.f : 0.f);
-      *reinterpret_cast<vecT*>(INVt + r * LDC + c0) = m;
+      st_2x8(INVt + r * LDC + c0, m);
     }
   }
   __syncthreads();
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
           vecT m;
 #pragma unroll
           for (int t = 0; t < VEC; ++t) m[t] = (r < len && c0 + t < len) ? iv[i][t] : from_f<T>(r == c0 + t ? 1.f : 0.f);
-          *reinterpret_cast<vecT*>(INVt + r * LDC + c0) = m;
+          st_2x8(INVt + r * LDC + c0, m);
           store_T_block(INVTt, LDC, 16 * (b % RT), 32 * (b / RT), m, lane);
         }
       } else {
@@ -654,13 +654,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         if (b < NBD) {
           int r, c;
           blk_rc(b, RT, r, c);
-          *reinterpret_cast<vecT*>(DoR + r * LDV + c) = dov[i];
+          st_2x8(DoR + r * LDV + c, dov[i]);
         }
       } else {
         const int vi = tid + i * NTH;
         if (vi < NVEC) {
           const int row = vi / (V / VEC), c8 = vi % (V / VEC);
-          *reinterpret_cast<vecT*>(DoR + row * LDV + c8 * VEC) = dov[i];
+          st_2x8(DoR + row * LDV + c8 * VEC, dov[i]);
         }
       }
     }
@@ -704,13 +704,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       const int kt = min(wave + ci * NW, KT - 1);
 #pragma unroll
       for (int kk = 0; kk < NKV; ++kk) {
-        bs[ci][kk] = frag_ld<T>(Sin, V, 16 * kt, kk * M::KS, lane);
+        bs[ci][kk] = frag_ld16<T>(Sin, V, 16 * kt, kk * M::KS, lane);
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int b = 0; b < 2; ++b)
             dsr[ci][kk][b] = *reinterpret_cast<const s4i*>(dSo + ScanFrag<K, V, C>::seed(2 * kk + b, kt, KT, lane));
         } else {
-          bd[ci][kk] = frag_ld<T>(dSo, V, 16 * kt, kk * M::KS, lane);
+          bd[ci][kk] = frag_ld16<T>(dSo, V, 16 * kt, kk * M::KS, lane);
         }
       }
     }
