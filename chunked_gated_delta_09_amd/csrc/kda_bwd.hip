@@ -268,7 +268,7 @@ struct GradLds {
   static constexpr size_t oMqkT = endB;
   static constexpr size_t oBeta = oMqkT + szCC;
   static constexpr size_t oDbp = oBeta + sizeof(float) * C;
-  static constexpr size_t oDoT = oDbp + sizeof(float) * NW * C;
+  static constexpr size_t oDoT = oDbp + sizeof(float) * 2 * NW * C;  // dbeta partials: dvc part, then phase-3 part
   // dg leaves through the dO slot in passes of SR rows of K fp32 (row stride K + 4)
   static constexpr int SR = C < 32 ? C : 32;
   static constexpr size_t total = mx(oDoT + szVC, oDoT + sizeof(float) * SR * (K + 4));
@@ -296,6 +296,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
   constexpr int VEC = 16 / (int)sizeof(T), NVEC = C * V / VEC, NDV = (NVEC + NTH - 1) / NTH;
   constexpr int LDK = Lay::LDK, LDC = Lay::LDC, LDV = Lay::LDV;
   constexpr int BN1 = VT % 2 == 0 ? 2 : 1;
+  static_assert(NW >= VT / BN1, "the blocks of one wave in the C x V walk lie in different row tiles");
   constexpr int NIT1 = (RT * (VT / BN1) + NW - 1) / NW;
   constexpr int NITC = (RT * RT + NW - 1) / NW;
   constexpr int NKV = V / M::KS;
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     // ---- phase 1: every global load of this value head, issued before any use
     // beta: loaded with the rest, written to LDS once everything is in flight
     const float beta_raw = bc[min(tid % C, len - 1) * s.HV];
-    for (int i = tid; i < NW * C; i += NTH) dbpart[i] = 0.f;
+    for (int i = tid; i < NW * C; i += NTH) dbpart[i] = 0.f;  // dvc part (written sparsely)
     float Gr[NCT][RT][4], qv[NCT][RT][4], kv[NCT][RT][4];
     ColTile<float, RT> tg[NCT];
     ColTile<T, RT> tq[NCT], tk[NCT];
@@ -682,11 +683,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
             store_rows<T>(Ndv, LDV, 16 * mt, 16 * (nt0 + jb), ndv, lane, 1 << 30);
             store_rows<T>(dvc_out, vs, 16 * mt, 16 * (nt0 + jb), dvb, lane, len);
           }
+          // row sums over the 16 columns; lane n < 4 writes row 4grp + n of the tile (each
+          // block of a wave has its own row tile, so these are plain writes)
+          float pw = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float p = row_allsum16(part[j]);
-            if (n == 0) dbpart[wave * C + 16 * mt + 4 * grp + j] += p;
+            pw = n == j ? p : pw;
           }
+          if (n < 4) dbpart[wave * C + 16 * mt + 4 * grp + n] = pw;
         }, wave, lane);
     __syncthreads();
 
@@ -745,6 +750,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     KDA_TS(2, 6);
     // ---- phase 3: per column tile of K, the C x K gradients of this value head
     float dGk[NCT][RT][4];
+    float dbz_sum[RT][4];  // dbeta part 2 row sums of this wave's column tiles
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dbz_sum[rt][j] = 0.f;
     // 16 x 16 identity as the B operand of a 16x16x16 bf16 MFMA (lane: column n, rows 4grp..)
     s4i ident4;
 #pragma unroll
@@ -828,10 +838,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
             store_rows<T>(dkc, qs, 16 * rt, 16 * kt, dk4, lane, len);
           }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p = row_allsum16(dbz[j]);
-            if (n == 0) dbpart[wave * C + 16 * rt + 4 * grp + j] += p;
-          }
+          for (int j = 0; j < 4; ++j) dbz_sum[rt][j] += row_allsum16(dbz[j]);
         }
         krd = col_allsum(krd);
         // dgam enters at the chunk's last valid row
@@ -879,12 +886,23 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         }
       }
     }
+    {
+      // lane n of group grp writes row 16(n/4) + 4grp + n%4 (plain write, every row once)
+      float v = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v = (n == 4 * rt + j) ? dbz_sum[rt][j] : v;
+      if (n < 4 * RT) dbpart[NW * C + wave * C + 16 * (n >> 2) + 4 * grp + (n & 3)] = v;
+    }
     __syncthreads();
     KDA_TS(2, 7);
     if (tid < len) {
       float acc = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) acc += dbpart[w * C + tid];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc += dbpart[NW * C + w * C + tid];
       dbc[tid * s.HV] = acc;
     }
     __syncthreads();
