@@ -20,7 +20,10 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled: plain float code is compiled to scalar VALU ops.
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-fPIC", "-fvisibility=hidden",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # MFMA accumulators in ordinary VGPRs: kernels with more than 256 registers per
+             # lane would otherwise keep them in AGPRs and copy them to VGPRs for every VALU use
+             "-mllvm", "-amdgpu-mfma-vgpr-form", "-I", INCLUDE, "-I", CSRC]
 
 
 def _hipcc() -> str:

@@ -154,112 +154,176 @@ __global__ __launch_bounds__(64) void scan_kernel(Shape s, const T* __restrict__
 }
 
 
-// bf16 path: the per-chunk operands are stored in fragment order (ScanFrag), so each wave
-// load is a contiguous 1 KB block, and the next chunk's operands are loaded into registers
-// while the current chunk is computed (the index is clamped, so the loads are
-// unconditional and always in flight). A second wave keeps the operands TOUCH_AHEAD chunks
-// further on moving into L2: one 4-byte load per 128-byte line, the lines shared by the
-// column slices of a head split between their workgroups, each load delivered into a
-// scratch word of LDS so that it holds no register and is never waited for. The two waves
-// meet at one barrier per chunk, which keeps the touches a fixed distance ahead.
+// bf16 path. The per-chunk operands P1, P2 (shared by every column slice of a (sequence,
+// head)) and e^gam are stored in fragment order (ScanFrag): each is a run of 1 KB wave
+// blocks. A workgroup holds NC column slices of one (sequence, head), one compute wave per
+// slice, plus two helper waves:
+//  - a copy wave streams the shared operands of chunk i+2 into a three-slot LDS ring
+//    (global_load_lds, 16 bytes per lane, no registers) while chunk i is computed, and
+//    waits for chunk i+1's copies to land before the barrier that opens step i+1;
+//  - a touch wave keeps the operands TOUCH_AHEAD chunks further on moving into L2 (one
+//    4-byte load per 128-byte line into a scratch LDS word, never waited for until exit).
+// All waves meet at one barrier per chunk step. The compute waves read the fragments from
+// LDS (contiguous 16-byte reads per lane) and load their own slice's seed tiles (W or Z)
+// from global memory one step ahead into a register double buffer. Pulling the shared
+// operands once per workgroup instead of once per slice is what sets the step time: a CU
+// moves only ~50 GB/s from L2.
 //
 // Backward direction: a column slice covers the columns ScanCols::col(vt, n) (not 16
 // consecutive ones), and the per-chunk dS leaves exactly as this wave holds it, 4 values
 // per lane and row tile in seed order (one 8-byte store per row tile); the gradient kernel
 // transposes it, and the column choice makes the transposed values of two slices one
 // contiguous B fragment.
-template <int K, int V, int C, bool FWD>
-__global__ __launch_bounds__(128) void scan_bf16_kernel(Shape s, const bf16* __restrict__ P1,
-                                                        const bf16* __restrict__ P2, const bf16* __restrict__ Zs,
-                                                        const bf16* __restrict__ Ws, const float* __restrict__ eg,
-                                                        const bf16* __restrict__ X0, bf16* __restrict__ Xout,
-                                                        bf16* __restrict__ Yout, float* __restrict__ Xfin) {
+// Ring slot layout, in 1 KB blocks: P1 fragments, P2 fragments, e^gam, then (SEED_DMA) the
+// seed tiles of the NC slices.
+template <int K, int V, int C, bool FWD, int NC>
+struct ScanRing {
   typedef ScanFrag<K, V, C> F;
+  static constexpr int NB1 = F::CT * F::KP, NB2 = F::KT * F::CQ;  // 1 KB blocks of P1, P2
+  static constexpr int OE = NB1 + NB2, OS = OE + 1;                 // e^gam block, first seed block
+  static constexpr int SROWS = FWD ? F::CT : F::KT;                 // 16-row seed tiles per slice
+  static constexpr bool SEED_DMA = NC <= 4 && SROWS % 2 == 0;       // seeds through the ring
+  static constexpr int SKB = SROWS / 2;                             // 1 KB blocks per slice's seeds
+  static constexpr int NL = OS + (SEED_DMA ? NC * SKB : 0);         // copies per chunk
+  static constexpr int SLOT = NL * 1024;
+  static constexpr int R = 3;  // ring slots
+  static_assert(NL <= 63, "the copy wave's wait count must fit vmcnt");
+  static_assert(K % 4 == 0 && K * 4 <= 1024, "e^gam fits one block");
+};
+
+template <int K, int V, int C, bool FWD, int NC>
+__global__ __launch_bounds__(64 * (NC + 2)) void scan_bf16_kernel(Shape s, const bf16* __restrict__ P1,
+                                                                  const bf16* __restrict__ P2, const bf16* __restrict__ Zs,
+                                                                  const bf16* __restrict__ Ws, const float* __restrict__ eg,
+                                                                  const bf16* __restrict__ X0, bf16* __restrict__ Xout,
+                                                                  bf16* __restrict__ Yout, float* __restrict__ Xfin) {
+  typedef ScanFrag<K, V, C> F;
+  typedef ScanRing<K, V, C, FWD, NC> RG;
   typedef Mma<bf16> M;
   constexpr int KT = F::KT, CT = F::CT, KP = F::KP, CQ = F::CQ, VT = V / 16;
   static_assert(KT % 2 == 0, "the bf16 scan pairs row tiles of X");
+  static_assert(VT % NC == 0, "a workgroup holds whole slices");
+  constexpr int NG = VT / NC;  // workgroups per (sequence, head)
+  // explicit read-ahead schedule of the ring (needs the registers of at most two waves per
+  // SIMD)
+  constexpr bool PIPE = NC <= 4;
+  __shared__ __align__(16) unsigned char ring[RG::R * RG::SLOT];
   // Workgroups are dealt round-robin to the 8 XCDs by linear id, so ids i, i+8, i+16, ...
-  // share an XCD (and its L2). All VT column slices of one (sequence, head) get ids of one
-  // residue class mod 8: the slices' shared per-chunk operands are then fetched from HBM
-  // once per XCD and served from L2 to the others.
+  // share an XCD (and its L2). The NG workgroups of one (sequence, head) get ids of one
+  // residue class mod 8: their shared per-chunk operands are fetched from HBM once per XCD.
   const int wid = blockIdx.x;
   const int xcd = wid % 8, r = wid / 8;
-  const int pair = (r / VT) * 8 + xcd;  // (sequence, head) index
-  const int vt = r % VT;
+  const int pair = (r / NG) * 8 + xcd;  // (sequence, head) index
+  const int vt0 = (r % NG) * NC;
   if (pair >= s.N * s.nhv) return;
   const int h = s.hv0 + pair % s.nhv, nseq = pair / s.nhv;
   const int lane = threadIdx.x & 63, n = lane & 15, grp = lane >> 4;
-  const int vcol = FWD ? 16 * vt + n : ScanCols::col(vt, n);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int c0, nc;
   seq_range(nseq, s.cu, s.choff, s.T, C, c0, nc);
   if (c0 + nc > s.NT) nc = max(0, s.NT - c0);
-  constexpr int TOUCH_AHEAD = 4;
+  auto chunk_of = [&](int ii) { return FWD ? c0 + ii : c0 + nc - 1 - ii; };
+  typedef const __attribute__((address_space(1))) void* gptr;
+  typedef __attribute__((address_space(3))) void* lptr;
 
-  if (threadIdx.x >= 64) {
-    // prefetch wave: lanes 0..31 cover this slice's share of the lines of P1 and P2,
-    // lanes 32..63 the lines of this slice's own seed tiles; a second load covers e^gam.
-    constexpr int SHARED_LINES = (F::P1_ELEMS + F::P2_ELEMS) * 2 / 128;
-    constexpr int SEED_LINES = (FWD ? C : K) * 16 * 2 / 128;
-    static_assert(SHARED_LINES <= 32 * VT && SEED_LINES <= 32, "one touch covers at most 64 lines per wave");
-    __shared__ int sink[64];
-    const int tl = min(32 * vt + (lane & 31), SHARED_LINES - 1);
-    const int tl2 = max(0, min(lane - 32, SEED_LINES - 1));
-    auto touch = [&](int c) {
-      const long ch = (long)c * s.HV + h;
-      const bf16* a;
-      if (lane < 32) {
-        a = tl < F::P1_ELEMS / 64 ? P1 + ch * F::P1_ELEMS + 64 * tl : P2 + ch * F::P2_ELEMS + 64 * (tl - F::P1_ELEMS / 64);
-      } else {
-        a = (FWD ? Zs + ch * C * V + F::seed(vt, 0, CT, 0) : Ws + ch * K * V + F::seed(vt, 0, KT, 0)) + 64 * tl2;
+  if (wave == NC) {
+    // copy wave: chunk index clamped to the last one, so every step issues exactly NL
+    // copies and the wait count below is exact
+    auto copy = [&](int ii) {
+      const long ch = (long)chunk_of(min(ii, nc - 1)) * s.HV + h;
+      unsigned char* slot = ring + (ii % RG::R) * RG::SLOT;
+      const bf16* p1 = P1 + ch * F::P1_ELEMS + 8 * lane;
+#pragma unroll
+      for (int b = 0; b < RG::NB1; ++b) __builtin_amdgcn_global_load_lds((gptr)(p1 + 512 * b), (lptr)(slot + 1024 * b), 16, 0, 0);
+      const bf16* p2 = P2 + ch * F::P2_ELEMS + 8 * lane;
+#pragma unroll
+      for (int b = 0; b < RG::NB2; ++b)
+        __builtin_amdgcn_global_load_lds((gptr)(p2 + 512 * b), (lptr)(slot + 1024 * (RG::NB1 + b)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr)(eg + ch * K + 4 * (lane % (K / 4))), (lptr)(slot + 1024 * RG::OE), 16, 0, 0);
+      if constexpr (RG::SEED_DMA) {
+        const bf16* sd = (FWD ? Zs + ch * C * V : Ws + ch * K * V) + 8 * lane;
+#pragma unroll
+        for (int w = 0; w < NC; ++w)
+#pragma unroll
+          for (int b = 0; b < RG::SKB; ++b)
+            __builtin_amdgcn_global_load_lds((gptr)(sd + F::seed(vt0 + w, 0, RG::SROWS, 0) + 512 * b),
+                                             (lptr)(slot + 1024 * (RG::OS + w * RG::SKB + b)), 16, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)a,
-                                       (__attribute__((address_space(3))) void*)sink, 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(eg + ch * K + 32 * (lane % ((K + 31) / 32))),
-                                       (__attribute__((address_space(3))) void*)sink, 4, 0, 0);
     };
-    for (int d = 1; d < TOUCH_AHEAD && d < nc; ++d) touch(FWD ? c0 + d : c0 + nc - 1 - d);
+    // Chunk j is copied into slot j % R during step j - 2, lands before the barrier that
+    // opens step j, and is read during that step.
+    if (nc > 0) {
+      copy(0);
+      copy(1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RG::NL) : "memory");  // chunk 0 landed
+    }
+    for (int ii = 0; ii < nc; ++ii) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // slot (ii + 2) % R was last read during step ii - 1
+      copy(ii + 2);
+      // chunk ii + 1 has landed (only the copies just issued may still be in flight)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RG::NL) : "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
+  if (wave == NC + 1) {
+    // touch wave: lanes cover this workgroup's share of the lines of P1 and P2 (split
+    // between the NG workgroups of the head), the lines of its slices' seed tiles, and e^gam
+    constexpr int TOUCH_AHEAD = 5;
+    constexpr int SHARED_LINES = (F::P1_ELEMS + F::P2_ELEMS) * 2 / 128;
+    constexpr int SH_PER = (SHARED_LINES + NG - 1) / NG;
+    constexpr int SEED_LINES = (FWD ? C : K) * 16 * 2 / 128;
+    constexpr int NLINES = SH_PER + NC * SEED_LINES + (K * 4 + 127) / 128;
+    __shared__ int sink[64];
+    const int vg = r % NG;
+    auto touch = [&](int ii) {
+      const long ch = (long)chunk_of(ii) * s.HV + h;
+#pragma unroll
+      for (int l0 = 0; l0 < NLINES; l0 += 64) {
+        const int l = min(l0 + lane, NLINES - 1);
+        const void* a;
+        if (l < SH_PER) {
+          const int sl = min(vg * SH_PER + l, SHARED_LINES - 1);
+          a = sl < F::P1_ELEMS / 64 ? (const void*)(P1 + ch * F::P1_ELEMS + 64 * sl)
+                                    : (const void*)(P2 + ch * F::P2_ELEMS + 64 * (sl - F::P1_ELEMS / 64));
+        } else if (l < SH_PER + NC * SEED_LINES) {
+          const int q = l - SH_PER, vt = vt0 + q / SEED_LINES, ql = q % SEED_LINES;
+          a = FWD ? (const void*)(Zs + ch * C * V + F::seed(vt, 0, CT, 0) + 64 * ql)
+                  : (const void*)(Ws + ch * K * V + F::seed(vt, 0, KT, 0) + 64 * ql);
+        } else {
+          a = eg + ch * K + 32 * (l - SH_PER - NC * SEED_LINES);
+        }
+        __builtin_amdgcn_global_load_lds((gptr)a, (lptr)sink, 4, 0, 0);
+      }
+    };
+    for (int d = 2; d < TOUCH_AHEAD && d < nc; ++d) touch(d);
     for (int ii = 0; ii < nc; ++ii) {
       __builtin_amdgcn_s_barrier();
-      if (ii + TOUCH_AHEAD < nc) touch(FWD ? c0 + ii + TOUCH_AHEAD : c0 + nc - 1 - ii - TOUCH_AHEAD);
+      if (ii + TOUCH_AHEAD < nc) touch(ii + TOUCH_AHEAD);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
   }
 
-  struct Ops {  // double-buffered: the next chunk's are loaded during the current step
-    bf16x8 a1[CT][KP];
-    bf16x8 a2[KT][CQ];
+  // ---- compute wave: slice vt of this (sequence, head)
+  const int vt = vt0 + wave;
+  const int vcol = FWD ? 16 * vt + n : ScanCols::col(vt, n);
+  struct Seed {  // this slice's seed tiles of one chunk: W (backward) or Z (forward)
+    bf16x4 t[FWD ? CT : KT];
   };
-  struct Small {  // loaded at the start of their own step, ahead of the next chunk's Ops
-    bf16x4 w[KT];
-    bf16x4 z[CT];
-    f32x4 e[KT];
-  };
-  auto load = [&](int c, Ops& o) {
-    const long ch = (long)c * s.HV + h;
-    const bf16x8* p1 = reinterpret_cast<const bf16x8*>(P1 + ch * F::P1_ELEMS) + lane;
-#pragma unroll
-    for (int m = 0; m < CT; ++m)
-#pragma unroll
-      for (int p = 0; p < KP; ++p) o.a1[m][p] = p1[(m * KP + p) * 64];
-    const bf16x8* p2 = reinterpret_cast<const bf16x8*>(P2 + ch * F::P2_ELEMS) + lane;
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-      for (int q = 0; q < CQ; ++q) o.a2[t][q] = p2[(t * CQ + q) * 64];
-  };
-  auto load_small = [&](int c, Small& o) {
-    const long ch = (long)c * s.HV + h;
-    if constexpr (!FWD) {
-#pragma unroll
-      for (int t = 0; t < KT; ++t) o.w[t] = *reinterpret_cast<const bf16x4*>(Ws + ch * K * V + F::seed(vt, t, KT, lane));
-    }
+  auto load_seed = [&](int ii, Seed& o) {
+    if constexpr (RG::SEED_DMA) return;  // read from the ring at its step instead
+    const long ch = (long)chunk_of(min(ii, nc - 1)) * s.HV + h;
     if constexpr (FWD) {
 #pragma unroll
-      for (int m = 0; m < CT; ++m) o.z[m] = *reinterpret_cast<const bf16x4*>(Zs + ch * C * V + F::seed(vt, m, CT, lane));
-    }
+      for (int m = 0; m < CT; ++m) o.t[m] = *reinterpret_cast<const bf16x4*>(Zs + ch * C * V + F::seed(vt, m, CT, lane));
+    } else {
 #pragma unroll
-    for (int t = 0; t < KT; ++t) o.e[t] = *reinterpret_cast<const f32x4*>(eg + ch * K + 16 * t + 4 * grp);
+      for (int t = 0; t < KT; ++t) o.t[t] = *reinterpret_cast<const bf16x4*>(Ws + ch * K * V + F::seed(vt, t, KT, lane));
+    }
   };
 
   f32x4 X[KT];
@@ -274,20 +338,63 @@ __global__ __launch_bounds__(128) void scan_bf16_kernel(Shape s, const bf16* __r
     for (int t = 0; t < KT; ++t) X[t] = zero4();
   }
 
-  // One chunk step with operands `cur`; the loads of the next chunk into `nxt` are issued
-  // first. The loop below alternates two buffers, so no register copy ever waits on a load
-  // still in flight.
-  auto step = [&](int ii, const Ops& cur, Ops& nxt) {
+  // One chunk step with this slice's seed tiles `cur`; the next step's go into `nxt`.
+  auto step = [&](int ii, const Seed& cur, Seed& nxt) {
+    // This wave's reads of the ring are complete before the barrier, after which the copy
+    // wave may refill a slot. The barrier is a plain one: the ring is written only by the
+    // copy wave, which waits for its own copies, and this wave's stores and seed loads may
+    // stay in flight across it.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    if (!FWD && ii < 63) KDA_TS(1, ii);
-    const int c = FWD ? c0 + ii : c0 + nc - 1 - ii;
-    Small sm;
-    load_small(c, sm);
-    {
-      const int in = min(ii + 1, nc - 1);
-      load(FWD ? c0 + in : c0 + nc - 1 - in, nxt);
+    asm volatile("" ::: "memory");
+    if constexpr (!RG::SEED_DMA) {
+      load_seed(ii + 1, nxt);
+      // keep the seed loads here, a whole step ahead of their use (the scheduler would
+      // otherwise sink them towards the end of the step)
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const long ch = (long)c * s.HV + h;
+    const long ch = (long)chunk_of(ii) * s.HV + h;
+    const unsigned char* slot = ring + (ii % RG::R) * RG::SLOT;
+    const bf16x8* a1 = reinterpret_cast<const bf16x8*>(slot) + lane;
+    const bf16x8* a2 = reinterpret_cast<const bf16x8*>(slot + 1024 * RG::NB1) + lane;
+    const float* eslot = reinterpret_cast<const float*>(slot + 1024 * RG::OE);
+    const bf16x4* sslot = reinterpret_cast<const bf16x4*>(slot + 1024 * (RG::OS + wave * RG::SKB)) + lane;
+
+    // With PIPE the ring is read in this program order -- forward: seed, P1 fragments,
+    // e^gam, P2 fragments; backward: P1 fragments, e^gam, seed, P2 fragments -- and the
+    // schedule at the end of the step issues each read well ahead of its use. Without PIPE
+    // the reads stay at their uses and the compiler schedules them.
+    bf16x8 f1[PIPE ? CT : 1][KP], f2[PIPE ? KT : 1][CQ];
+    f32x4 ev[PIPE ? KT : 1];
+    bf16x4 sd[RG::SEED_DMA ? RG::SROWS : 1];
+    auto read_seed = [&]() {
+      if constexpr (RG::SEED_DMA) {
+#pragma unroll
+        for (int i = 0; i < RG::SROWS; ++i) sd[i] = sslot[64 * i];
+      }
+    };
+    if constexpr (PIPE) {
+      if constexpr (FWD) read_seed();
+#pragma unroll
+      for (int m = 0; m < CT; ++m)
+#pragma unroll
+        for (int p = 0; p < KP; ++p) f1[m][p] = a1[(m * KP + p) * 64];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) ev[t] = *reinterpret_cast<const f32x4*>(eslot + 16 * t + 4 * grp);
+      if constexpr (!FWD) read_seed();
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int q = 0; q < CQ; ++q) f2[t][q] = a2[(t * CQ + q) * 64];
+    } else {
+      read_seed();
+    }
+    auto F1 = [&](int m, int p) { if constexpr (PIPE) return f1[m][p]; else return a1[(m * KP + p) * 64]; };
+    auto F2 = [&](int t, int q) { if constexpr (PIPE) return f2[t][q]; else return a2[(t * CQ + q) * 64]; };
+    auto EV = [&](int t) {
+      if constexpr (PIPE) return ev[t]; else return *reinterpret_cast<const f32x4*>(eslot + 16 * t + 4 * grp);
+    };
+    auto SD = [&](int i) { if constexpr (RG::SEED_DMA) return sd[i]; else return cur.t[i]; };
 
     bf16x8 bx[KP];
 #pragma unroll
@@ -316,7 +423,8 @@ __global__ __launch_bounds__(128) void scan_bf16_kernel(Shape s, const bf16* __r
 #pragma unroll
     for (int m = 0; m < CT; ++m) {
       if constexpr (FWD) {
-        Y[m] = f32x4{(float)sm.z[m][0], (float)sm.z[m][1], (float)sm.z[m][2], (float)sm.z[m][3]};
+        const bf16x4 z = SD(m);
+        Y[m] = f32x4{(float)z[0], (float)z[1], (float)z[2], (float)z[3]};
       } else {
         Y[m] = zero4();
       }
@@ -324,62 +432,64 @@ __global__ __launch_bounds__(128) void scan_bf16_kernel(Shape s, const bf16* __r
 #pragma unroll
     for (int p = 0; p < KP; ++p)
 #pragma unroll
-      for (int m = 0; m < CT; ++m) Y[m] = M::mma(cur.a1[m][p], bx[p], Y[m]);
+      for (int m = 0; m < CT; ++m) Y[m] = M::mma(F1(m, p), bx[p], Y[m]);
     if constexpr (!FWD) {
 #pragma unroll
       for (int m = 0; m < CT; ++m) st4(Yout + ch * V * C + vcol * C + 16 * m + 4 * grp, Y[m]);
     }
 
-    // X' = W + P2 Y;  X = diag(e^gam) X + X'
-    f32x4 Xn[KT];
+    // X = diag(e^gam) X + W + P2 Y, accumulated in place (X itself is no longer needed: Y
+    // used its bf16 copy)
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
+      X[t] = EV(t) * X[t];
       if constexpr (!FWD) {
-        Xn[t] = f32x4{(float)sm.w[t][0], (float)sm.w[t][1], (float)sm.w[t][2], (float)sm.w[t][3]};
-      } else {
-        Xn[t] = zero4();
+        const bf16x4 w = SD(t);
+        X[t] += f32x4{(float)w[0], (float)w[1], (float)w[2], (float)w[3]};
       }
     }
 #pragma unroll
     for (int q = 0; q < CQ; ++q) {
-      const bool pair = 2 * q + 1 < CT;
+      const bool pair2 = 2 * q + 1 < CT;
       bf16x8 b;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         b[i] = (bf16)Y[2 * q][i];
-        b[4 + i] = pair ? (bf16)Y[pair ? 2 * q + 1 : 2 * q][i] : (bf16)0.0f;
+        b[4 + i] = pair2 ? (bf16)Y[pair2 ? 2 * q + 1 : 2 * q][i] : (bf16)0.0f;
       }
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
-        bf16x8 a = cur.a2[t][q];
-        if (!pair) {
+        bf16x8 a = F2(t, q);
+        if (!pair2) {
 #pragma unroll
           for (int i = 4; i < 8; ++i) a[i] = (bf16)0.0f;
         }
-        Xn[t] = M::mma(a, b, Xn[t]);
+        X[t] = M::mma(a, b, X[t]);
       }
     }
+    if constexpr (PIPE) {
+      // the first UP ring reads (at least everything the first product needs), then one
+      // further read after each MFMA: every read is issued at least 8 MFMAs before its use
+      constexpr int NR = CT * KP + KT + KT * CQ + (RG::SEED_DMA ? RG::SROWS : 0), NMMA = CT * KP + KT * CQ;
+      constexpr int PRE = CT * KP + (FWD && RG::SEED_DMA ? RG::SROWS : 0);
+      constexpr int UP = PRE > NR - NMMA + 8 ? PRE : NR - NMMA + 8;
+      static_assert(UP <= NR && NR - UP <= NMMA, "the interleave covers every ring read");
+      __builtin_amdgcn_sched_group_barrier(0x100, UP, 0);
 #pragma unroll
-    for (int t = 0; t < KT; ++t) X[t] = sm.e[t] * X[t] + Xn[t];
-    // Issue order: this step's small loads first, then one load of the next chunk's
-    // fragments after each MFMA, so that the address unit works while the matrix pipe does
-    // (issued as one burst, the loads would hold up the MFMAs behind them).
-    constexpr int NSMALL = KT + (FWD ? CT : KT), NMMA = CT * KP + KT * CQ;
-    static_assert(NMMA == CT * KP + KT * CQ, "one next-chunk load per MFMA");
-    __builtin_amdgcn_sched_group_barrier(0x020, NSMALL, 0);
-#pragma unroll
-    for (int i = 0; i < NMMA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      for (int i = 0; i < NR - UP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMMA - (NR - UP), 0);
     }
   };
 
   if (nc > 0) {
-    Ops ping, pong;
-    load(FWD ? c0 : c0 + nc - 1, ping);
+    Seed sa, sb;
+    load_seed(0, sa);
     for (int ii = 0; ii < nc; ii += 2) {
-      step(ii, ping, pong);
-      if (ii + 1 < nc) step(ii + 1, pong, ping);
+      step(ii, sa, sb);
+      if (ii + 1 < nc) step(ii + 1, sb, sa);
     }
   }
 
@@ -397,12 +507,21 @@ static hipError_t scan_t(const Shape& s, const void* P1, const void* P2, const v
                          const float* eg, const void* X0, void* Xout, void* Yout, float* Xfin, hipStream_t st) {
   if (s.N == 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    const int pairs = s.N * s.nhv;
-    const int grid = ((pairs + 7) / 8) * 8 * (V / 16);
-    hipLaunchKernelGGL((scan_bf16_kernel<K, V, C, FWD>), dim3(grid), dim3(128), 0, st, s,
-                       static_cast<const bf16*>(P1), static_cast<const bf16*>(P2), static_cast<const bf16*>(Zi),
-                       static_cast<const bf16*>(Wi), eg, static_cast<const bf16*>(X0), static_cast<bf16*>(Xout),
-                       static_cast<bf16*>(Yout), Xfin);
+    // Slices per workgroup: the fewest that keep the grid within about one workgroup per CU
+    // (the ring takes ~100 KB of LDS); more slices share one pull of the operands.
+    const int pairs = s.N * s.nhv, slices = pairs * (V / 16);
+    int nc = 1;
+    while (nc < V / 16 && slices / nc > 256) nc *= 2;
+    const int grid = ((pairs + 7) / 8) * 8 * (V / 16 / nc);
+    auto go = [&](auto kern, int ncw) {
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (ncw + 2)), 0, st, s, static_cast<const bf16*>(P1),
+                         static_cast<const bf16*>(P2), static_cast<const bf16*>(Zi), static_cast<const bf16*>(Wi), eg,
+                         static_cast<const bf16*>(X0), static_cast<bf16*>(Xout), static_cast<bf16*>(Yout), Xfin);
+    };
+    if (nc == 1) go(scan_bf16_kernel<K, V, C, FWD, 1>, 1);
+    else if (nc == 2) go(scan_bf16_kernel<K, V, C, FWD, 2>, 2);
+    else if (nc == 4) go(scan_bf16_kernel<K, V, C, FWD, 4>, 4);
+    else go(scan_bf16_kernel<K, V, C, FWD, 8>, 8);
   } else {
     hipLaunchKernelGGL((scan_kernel<T, K, V, C, FWD>), dim3(V / 16, s.nhv, s.N), dim3(64), 0, st, s,
                        static_cast<const T*>(P1), static_cast<const T*>(P2), static_cast<const T*>(Zi),
