@@ -174,6 +174,21 @@ __global__ __launch_bounds__(64) void scan_kernel(Shape s, const T* __restrict__
 // per lane and row tile in seed order (one 8-byte store per row tile); the gradient kernel
 // transposes it, and the column choice makes the transposed values of two slices one
 // contiguous B fragment.
+// Global -> LDS copies (lane i's bytes land at lds + i * bytes). Issued as inline assembly:
+// the compiler's wait insertion would otherwise treat every LDS read of the ring as
+// depending on these copies and make the reading wave wait for all of its own outstanding
+// global stores. The copying wave waits for its copies explicitly (vmcnt) before the barrier
+// that hands them over.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+__device__ __forceinline__ void copy16_to_lds(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory", "m0");
+}
+
 // Ring slot layout, in 1 KB blocks: P1 fragments, P2 fragments, e^gam, then (SEED_DMA) the
 // seed tiles of the NC slices.
 template <int K, int V, int C, bool FWD, int NC>
@@ -223,8 +238,6 @@ __global__ __launch_bounds__(64 * (NC + 2)) void scan_bf16_kernel(Shape s, const
   seq_range(nseq, s.cu, s.choff, s.T, C, c0, nc);
   if (c0 + nc > s.NT) nc = max(0, s.NT - c0);
   auto chunk_of = [&](int ii) { return FWD ? c0 + ii : c0 + nc - 1 - ii; };
-  typedef const __attribute__((address_space(1))) void* gptr;
-  typedef __attribute__((address_space(3))) void* lptr;
 
   if (wave == NC) {
     // copy wave: chunk index clamped to the last one, so every step issues exactly NL
@@ -234,20 +247,19 @@ __global__ __launch_bounds__(64 * (NC + 2)) void scan_bf16_kernel(Shape s, const
       unsigned char* slot = ring + (ii % RG::R) * RG::SLOT;
       const bf16* p1 = P1 + ch * F::P1_ELEMS + 8 * lane;
 #pragma unroll
-      for (int b = 0; b < RG::NB1; ++b) __builtin_amdgcn_global_load_lds((gptr)(p1 + 512 * b), (lptr)(slot + 1024 * b), 16, 0, 0);
+      for (int b = 0; b < RG::NB1; ++b) copy16_to_lds(p1 + 512 * b, slot + 1024 * b);
       const bf16* p2 = P2 + ch * F::P2_ELEMS + 8 * lane;
 #pragma unroll
       for (int b = 0; b < RG::NB2; ++b)
-        __builtin_amdgcn_global_load_lds((gptr)(p2 + 512 * b), (lptr)(slot + 1024 * (RG::NB1 + b)), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gptr)(eg + ch * K + 4 * (lane % (K / 4))), (lptr)(slot + 1024 * RG::OE), 16, 0, 0);
+        copy16_to_lds(p2 + 512 * b, slot + 1024 * (RG::NB1 + b));
+      copy16_to_lds(eg + ch * K + 4 * (lane % (K / 4)), slot + 1024 * RG::OE);
       if constexpr (RG::SEED_DMA) {
         const bf16* sd = (FWD ? Zs + ch * C * V : Ws + ch * K * V) + 8 * lane;
 #pragma unroll
         for (int w = 0; w < NC; ++w)
 #pragma unroll
           for (int b = 0; b < RG::SKB; ++b)
-            __builtin_amdgcn_global_load_lds((gptr)(sd + F::seed(vt0 + w, 0, RG::SROWS, 0) + 512 * b),
-                                             (lptr)(slot + 1024 * (RG::OS + w * RG::SKB + b)), 16, 0, 0);
+            copy16_to_lds(sd + F::seed(vt0 + w, 0, RG::SROWS, 0) + 512 * b, slot + 1024 * (RG::OS + w * RG::SKB + b));
       }
     };
     // Chunk j is copied into slot j % R during step j - 2, lands before the barrier that
@@ -296,7 +308,7 @@ __global__ __launch_bounds__(64 * (NC + 2)) void scan_bf16_kernel(Shape s, const
         } else {
           a = eg + ch * K + 32 * (l - SH_PER - NC * SEED_LINES);
         }
-        __builtin_amdgcn_global_load_lds((gptr)a, (lptr)sink, 4, 0, 0);
+        copy4_to_lds(a, sink);
       }
     };
     for (int d = 2; d < TOUCH_AHEAD && d < nc; ++d) touch(d);
