@@ -209,6 +209,26 @@ def main():
     _, cold_kern, _ = timed(args.steps, flush=True, per_kernel=True)
     _, warm_kern, _ = timed(args.steps, flush=False, per_kernel=True)
 
+    # The training forward (kda_fwd_states with the output o), timed the same way (cold):
+    # reported beside the backward, not part of the step.
+    def fwd_step():
+        return kda.fwd_states(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], cu_seqlens=inp["cu_seqlens"],
+                              C=w.C, scale=inp["scale"], output_o=True)
+
+    for _ in range(2):
+        fwd_step()
+    fwd_ev = new_events(2 * args.steps)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        flush_buf.fill_(i & 0xFF)
+        hip.hipEventRecord(fwd_ev[2 * i], stream)
+        fwd_step()
+        hip.hipEventRecord(fwd_ev[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    fwd_ms = statistics.mean(elapsed(fwd_ev[2 * i], fwd_ev[2 * i + 1]) for i in range(args.steps))
+    for e in fwd_ev:
+        hip.hipEventDestroy(e)
+
     th = B * T * w.HV
     ms = statistics.mean(cold_calls)
     value = th / (ms * 1e-3)
@@ -246,6 +266,8 @@ def main():
                                          statistics.median(cold_calls),
                                          sorted(cold_calls)[int(0.9 * (len(cold_calls) - 1))]],
         "ms_per_step_warm": statistics.mean(warm_calls),
+        "forward": {"entry": "kda_fwd_states with o (chunk prep, forward state scan, output)",
+                    "ms_cold": fwd_ms, "token_heads_per_s": th / (fwd_ms * 1e-3)},
         "wall_s_timed_cold_incl_flush": cold_wall,
     }
     if not args.no_cpu_baseline:

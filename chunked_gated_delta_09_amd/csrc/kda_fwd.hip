@@ -42,103 +42,182 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
   }
 }
 
+// LDS plan of the forward prep kernel (two workgroups per CU). Later buffers overlay
+// earlier ones that a barrier has retired:
+//   Kd, Ki (until L)                 -> X (fp32 inverse) and INV (bf16 / fp32 operand)
+//   L (fp32, until the inverse)      -> diag(beta) v^T
+//   diag(beta) kd^T (whole kernel)
 template <class T, int K, int V, int C>
 struct FwdPrepLds {
   static constexpr int P = pad_of<T>();
   static constexpr int LDK = K + P, LDC = C + P, LDL = C + 4;
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t oKd = 0;
   static constexpr size_t oKi = oKd + sizeof(T) * C * LDK;
-  static constexpr size_t oBKdT = oKi + sizeof(T) * C * LDK;
-  static constexpr size_t oBVT = oBKdT + sizeof(T) * K * LDC;
-  static constexpr size_t oL = oBVT + sizeof(T) * V * LDC;
-  static constexpr size_t oINV = oL + sizeof(float) * C * LDL;
-  static constexpr size_t oBeta = oINV + sizeof(T) * C * LDC;
+  static constexpr size_t oX = 0;
+  static constexpr size_t oINV = oX + sizeof(float) * C * LDL;
+  static constexpr size_t endA = mx(oKi + sizeof(T) * C * LDK, oINV + sizeof(T) * C * LDC);
+  static constexpr size_t oBKdT = endA;
+  static constexpr size_t oL = oBKdT + sizeof(T) * K * LDC;
+  static constexpr size_t oBVT = oL;
+  static constexpr size_t oBeta = oL + mx(sizeof(float) * C * LDL, sizeof(T) * V * LDC);
   static constexpr size_t total = oBeta + sizeof(float) * C;
+  static_assert(total <= 80 * 1024 || C > 64, "two workgroups per CU");
 };
 
-// One workgroup per (chunk, value head).
+// (I + L)^-1 of a unit lower-triangular C x C matrix (L strictly lower, fp32 in LDS with row
+// stride LDL), blocked by 16: each diagonal block is inverted by forward substitution (one
+// wave, a lane per column), then the blocks below the diagonal follow one block diagonal at
+// a time, X_ij = -X_ii * sum_{k=j..i-1} L_ik X_kj, as fp32 16x16x4 MFMA products (a block per
+// wave). X (fp32, same stride) receives the inverse; its upper triangle is zero. Whole
+// workgroup; begins and ends with every wave's LDS writes visible.
+template <int C, int NW>
+__device__ __forceinline__ void unit_lower_inverse(const float* __restrict__ L, float* __restrict__ X, int ldl,
+                                                   int wave, int lane) {
+  constexpr int RT = C / 16;
+  static_assert(NW >= RT, "a wave per diagonal block");
+  const int n = lane & 15, grp = lane >> 4;
+  // diagonal blocks; the rest of the upper triangle is cleared by the same waves
+  if (wave < RT) {
+    const int b = 16 * wave;
+    if (lane < 16) {
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = i == lane ? 1.f : 0.f;
+        const float* Lrow = L + (b + i) * ldl + b;
+#pragma unroll
+        for (int j = 0; j < i; ++j) acc -= Lrow[j] * x[j];
+        x[i] = acc;
+        X[(b + i) * ldl + b + lane] = acc;
+      }
+    }
+    // blocks above the diagonal in this block row are zero
+    for (int cb = wave + 1; cb < RT; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) X[(b + 4 * grp + j) * ldl + 16 * cb + n] = 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int d = 1; d < RT; ++d) {
+    const int i = d + wave, j = wave;  // block (i, j) on block diagonal d
+    if (i < RT) {
+      // S = sum_k L_ik X_kj (standard contraction order)
+      f32x4 S = zero4();
+      for (int k = j; k < i; ++k)
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4)
+          S = __builtin_amdgcn_mfma_f32_16x16x4f32(L[(16 * i + n) * ldl + 16 * k + k0 + grp],
+                                                   X[(16 * k + k0 + grp) * ldl + 16 * j + n], S, 0, 0, 0);
+      // X_ij = -X_ii S, with the contraction index permuted so that S's accumulator values are
+      // the B operand as held: step s covers contraction indices 4g + s (lane group g)
+      f32x4 D = zero4();
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        D = __builtin_amdgcn_mfma_f32_16x16x4f32(X[(16 * i + n) * ldl + 16 * i + 4 * grp + st], S[st], D, 0, 0, 0);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) X[(16 * i + 4 * grp + jj) * ldl + 16 * j + n] = -D[jj];
+    }
+    __syncthreads();
+  }
+}
+
+// One workgroup per (chunk, value head); 512 threads, two workgroups per CU.
 template <class T, int K, int V, int C>
-__global__ __launch_bounds__(256) void fwd_prep_kernel(Shape s, const T* __restrict__ kp, const T* __restrict__ vp,
-                                                        const float* __restrict__ gp, const float* __restrict__ bp,
-                                                        T* __restrict__ invp, FwdWs ws) {
+__global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __restrict__ kp, const T* __restrict__ vp,
+                                                           const float* __restrict__ gp, const float* __restrict__ bp,
+                                                           T* __restrict__ invp, FwdWs ws) {
   typedef FwdPrepLds<T, K, V, C> Lay;
-  constexpr int NW = 4, RT = C / 16, KT = K / 16, VT = V / 16;
+  constexpr int NW = 8, RT = C / 16, KT = K / 16, VT = V / 16;
+  constexpr int NCK = (KT + NW - 1) / NW, NCV = (VT + NW - 1) / NW;
   constexpr int LDK = Lay::LDK, LDC = Lay::LDC, LDL = Lay::LDL;
   __shared__ __align__(16) unsigned char smem[Lay::total];
   T* Kd = reinterpret_cast<T*>(smem + Lay::oKd);
   T* Ki = reinterpret_cast<T*>(smem + Lay::oKi);
-  T* BKdT = reinterpret_cast<T*>(smem + Lay::oBKdT);
-  T* BVT = reinterpret_cast<T*>(smem + Lay::oBVT);
-  float* Lf = reinterpret_cast<float*>(smem + Lay::oL);
+  float* Xf = reinterpret_cast<float*>(smem + Lay::oX);
   T* INVt = reinterpret_cast<T*>(smem + Lay::oINV);
+  T* BKdT = reinterpret_cast<T*>(smem + Lay::oBKdT);
+  float* Lf = reinterpret_cast<float*>(smem + Lay::oL);
+  T* BVT = reinterpret_cast<T*>(smem + Lay::oBVT);
   float* betas = reinterpret_cast<float*>(smem + Lay::oBeta);
 
   const int c = blockIdx.x, h = s.hv0 + blockIdx.y;
   const int hq = h / (s.HV / s.H);
   const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long ch = (long)c * s.HV + h;
   const int len = geo.len;
   if (len <= 0) return;
   const int qs = s.H * K, gs = s.HV * K, vs = s.HV * V;
-  const T* kc = kp + (geo.bos * s.H + hq) * K;
-  const float* gc = gp + (geo.bos * s.HV + h) * K;
-  const T* vc = vp + (geo.bos * s.HV + h) * V;
-  const float* bc = bp + geo.bos * s.HV + h;
+  const T* __restrict__ kc = kp + (geo.bos * s.H + hq) * K;
+  const float* __restrict__ gc = gp + (geo.bos * s.HV + h) * K;
+  const T* __restrict__ vc = vp + (geo.bos * s.HV + h) * V;
+  const float* __restrict__ bc = bp + geo.bos * s.HV + h;
 
-  if (tid < C) betas[tid] = tid < len ? bc[tid * s.HV] : 0.f;
+  // ---- every global load, issued before any use (row pieces, moved to the column-owner
+  // layout by the tiles' MFMA transposes)
+  const float beta_raw = bc[min(tid % C, len - 1) * s.HV];
+  ColTile<float, RT> tg[NCK];
+  ColTile<T, RT> tk[NCK], tv[NCV];
+#pragma unroll
+  for (int ci = 0; ci < NCK; ++ci) {
+    const int kt = min(wave + ci * NW, KT - 1);
+    tg[ci].load(gc, gs, 16 * kt, lane, len);
+    tk[ci].load(kc, qs, 16 * kt, lane, len);
+  }
+#pragma unroll
+  for (int cv = 0; cv < NCV; ++cv) tv[cv].load(vc, vs, 16 * min(wave + cv * NW, VT - 1), lane, len);
+  if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
   __syncthreads();
 
-  for (int kt = wave; kt < KT; kt += NW) {
-    const int col = 16 * kt + n;
-    float G[RT][4];
+  // ---- gate cumsum; kd, ki (row-major), diag(beta) kd^T, kr (scan fragment order), e^gam
+  T* __restrict__ krT = reinterpret_cast<T*>(ws.krT) + ch * (sizeof(T) == 2 ? ScanFrag<K, V, C>::P2_ELEMS : K * C);
+#pragma unroll
+  for (int ci = 0; ci < NCK; ++ci) {
+    const int kt = wave + ci * NW;
+    if (kt < KT) {
+      float G[RT][4], kv[RT][4];
+      tg[ci].get(G, lane, len);
+      tk[ci].get(kv, lane, len);
+      const int col = 16 * kt + n;
+      const float gam = col_prefix<RT>(G, lane);  // the column total is gam
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 kd4, ki4, bk, kr4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * rt + 4 * grp + j;
+          const float e = __expf(G[rt][j]);
+          kd4[j] = kv[rt][j] * e;
+          ki4[j] = kv[rt][j] * __expf(-G[rt][j]);
+          bk[j] = betas[row] * kd4[j];
+          kr4[j] = kv[rt][j] * __expf(gam - G[rt][j]);
+        }
+        store_rows<T>(Kd, LDK, 16 * rt, 16 * kt, kd4, lane, 1 << 30);
+        store_rows<T>(Ki, LDK, 16 * rt, 16 * kt, ki4, lane, 1 << 30);
+        st4(BKdT + col * LDC + 16 * rt + 4 * grp, bk);
+        if constexpr (sizeof(T) == 2) {
+          st4(krT + ScanFrag<K, V, C>::p2(col, 16 * rt + 4 * grp), kr4);
+        } else {
+          st4(krT + col * C + 16 * rt + 4 * grp, kr4);
+        }
+      }
+      if (grp == 0) ws.eg[ch * K + col] = __expf(gam);
+    }
+  }
+  float bv[NCV][RT][4];  // diag(beta) v in the column-owner layout, stored once L is retired
+#pragma unroll
+  for (int cv = 0; cv < NCV; ++cv) {
+    tv[cv].get(bv[cv], lane, len);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rt + 4 * grp + j;
-        G[rt][j] = row < len ? gc[row * gs + col] : 0.f;
-      }
-    const float gam = col_prefix<RT>(G, lane);  // the column total is gam
-    T* __restrict__ krT = reinterpret_cast<T*>(ws.krT) + ch * (sizeof(T) == 2 ? ScanFrag<K, V, C>::P2_ELEMS : K * C);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 bk, kr4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rt + 4 * grp + j;
-        const float kv = row < len ? to_f(kc[row * qs + col]) : 0.f;
-        const float kd = kv * __expf(G[rt][j]);
-        Kd[row * LDK + col] = from_f<T>(kd);
-        Ki[row * LDK + col] = from_f<T>(kv * __expf(-G[rt][j]));
-        bk[j] = betas[row] * kd;
-        kr4[j] = kv * __expf(gam - G[rt][j]);
-      }
-      st4(BKdT + col * LDC + 16 * rt + 4 * grp, bk);
-      if constexpr (sizeof(T) == 2) {
-        st4(krT + ScanFrag<K, V, C>::p2(col, 16 * rt + 4 * grp), kr4);
-      } else {
-        st4(krT + col * C + 16 * rt + 4 * grp, kr4);
-      }
-    }
-    if (grp == 0) ws.eg[ch * K + col] = __expf(gam);
-  }
-  for (int vt = wave; vt < VT; vt += NW) {
-    const int col = 16 * vt + n;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 bv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rt + 4 * grp + j;
-        bv[j] = row < len ? betas[row] * to_f(vc[row * vs + col]) : 0.f;
-      }
-      st4(BVT + col * LDC + 16 * rt + 4 * grp, bv);
-    }
+      for (int j = 0; j < 4; ++j) bv[cv][rt][j] *= betas[16 * rt + 4 * grp + j];
   }
   __syncthreads();
 
-  // L = strict_tril(diag(beta) kd ki^T), fp32.
+  // ---- L = strict_tril(diag(beta) kd ki^T), fp32
   block_gemm<T, RT, RT, 1, NW, K>(
       Kd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
       [&](int, int mt, int nt0, f32x4(&acc)[1]) {
@@ -148,24 +227,26 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(Shape s, const T* __restr
           Lf[row * LDL + col] = col < row ? betas[row] * acc[0][j] : 0.f;
         }
       }, wave, lane);
-  __syncthreads();
+  __syncthreads();  // Kd, Ki retired (the epilogue also wrote the skipped upper blocks as zero)
 
-  // INV = (I + L)^-1 by forward substitution in fp32, one thread per column:
-  // X[i][col] = delta(i, col) - sum_{j<i} L[i][j] X[j][col].
-  if (tid < C) {
-    const int col = tid;
-    float x[C];
-    T* inv = invp + ch * C * C;
+  // ---- INV = (I + L)^-1 (fp32, into the Kd/Ki region)
+  unit_lower_inverse<C, NW>(Lf, Xf, LDL, wave, lane);
+
+  // ---- INV to global memory and as the MFMA operand; diag(beta) v^T over L
+  T* __restrict__ inv = invp + ch * C * C;
+  for (int i = tid; i < C * C / 4; i += 64 * NW) {
+    const int row = (4 * i) / C, col = (4 * i) % C;
+    const f32x4 x4 = *reinterpret_cast<const f32x4*>(Xf + row * LDL + col);
+    st4(inv + row * C + col, x4);
+    st4(INVt + row * LDC + col, x4);
+  }
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      float acc = i == col ? 1.f : 0.f;
-      const float* Lrow = Lf + i * LDL;
+  for (int cv = 0; cv < NCV; ++cv) {
+    const int vt = wave + cv * NW;
+    if (vt < VT) {
 #pragma unroll
-      for (int j = 0; j < i; ++j) acc -= Lrow[j] * x[j];
-      x[i] = acc;
-      const T xt = from_f<T>(acc);
-      inv[i * C + col] = xt;
-      INVt[i * LDC + col] = xt;
+      for (int rt = 0; rt < RT; ++rt)
+        st4(BVT + (16 * vt + n) * LDC + 16 * rt + 4 * grp, f32x4{bv[cv][rt][0], bv[cv][rt][1], bv[cv][rt][2], bv[cv][rt][3]});
     }
   }
   __syncthreads();
@@ -214,18 +295,27 @@ struct FwdOutLds {
   static constexpr size_t oUT = oMqk + sizeof(T) * C * LDC;
   static constexpr size_t oBeta = oUT + sizeof(T) * V * LDC;
   static constexpr size_t total = oBeta + sizeof(float) * C;
+  static_assert(total <= 160 * 1024, "output kernel exceeds the LDS of one CU");
 };
 
 // o = qd S_in + tril(qd ki^T) U with U = INV diag(beta)(v - kd S_in); one workgroup per
-// (chunk, value head).
+// (chunk, value head), 512 threads. Every global load is issued before any use: g, q, k and
+// v as row pieces moved to the column-owner layout by MFMA transposes, S_in and INV as
+// 16-byte pieces (bf16: 16 x 32 blocks, written transposed into LDS by MFMA transposes).
 template <class T, int K, int V, int C>
-__global__ __launch_bounds__(256) void fwd_out_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
+__global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
                                                        const T* __restrict__ vp, const float* __restrict__ gp,
                                                        const float* __restrict__ bp, const T* __restrict__ states,
                                                        const T* __restrict__ invp, T* __restrict__ op) {
   typedef FwdOutLds<T, K, V, C> Lay;
-  constexpr int NW = 4, RT = C / 16, KT = K / 16, VT = V / 16;
+  typedef T vecT __attribute__((ext_vector_type(16 / sizeof(T))));
+  typedef T t4 __attribute__((ext_vector_type(4)));
+  constexpr int NW = 8, NTH = 64 * NW, RT = C / 16, KT = K / 16, VT = V / 16;
+  constexpr int NCK = (KT + NW - 1) / NW;
+  constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int LDK = Lay::LDK, LDC = Lay::LDC;
+  constexpr int BN = VT % 2 == 0 ? 2 : 1;
+  constexpr int NIT1 = (RT * (VT / BN) + NW - 1) / NW;
   __shared__ __align__(16) unsigned char smem[Lay::total];
   T* Qd = reinterpret_cast<T*>(smem + Lay::oQd);
   T* Kd = reinterpret_cast<T*>(smem + Lay::oKd);
@@ -240,92 +330,183 @@ __global__ __launch_bounds__(256) void fwd_out_kernel(Shape s, const T* __restri
   const int c = blockIdx.x, h = s.hv0 + blockIdx.y;
   const int hq = h / (s.HV / s.H);
   const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long ch = (long)c * s.HV + h;
   const int len = geo.len;
   if (len <= 0) return;
   const int qs = s.H * K, gs = s.HV * K, vs = s.HV * V;
-  const T* qc = qp + (geo.bos * s.H + hq) * K;
-  const T* kc = kp + (geo.bos * s.H + hq) * K;
-  const float* gc = gp + (geo.bos * s.HV + h) * K;
-  const T* vc = vp + (geo.bos * s.HV + h) * V;
-  T* oc = op + (geo.bos * s.HV + h) * V;
-  const float* bc = bp + geo.bos * s.HV + h;
+  const T* __restrict__ qc = qp + (geo.bos * s.H + hq) * K;
+  const T* __restrict__ kc = kp + (geo.bos * s.H + hq) * K;
+  const float* __restrict__ gc = gp + (geo.bos * s.HV + h) * K;
+  const T* __restrict__ vc = vp + (geo.bos * s.HV + h) * V;
+  T* __restrict__ oc = op + (geo.bos * s.HV + h) * V;
+  const float* __restrict__ bc = bp + geo.bos * s.HV + h;
+  const T* __restrict__ Sin = states + ch * K * V;
+  const T* __restrict__ invc = invp + ch * C * C;
 
-  if (tid < C) betas[tid] = tid < len ? bc[tid * s.HV] : 0.f;
-  for (int kt = wave; kt < KT; kt += NW) {
-    const int col = 16 * kt + n;
-    float G[RT][4];
+  // ---- loads
+  const float beta_raw = bc[min(tid % C, len - 1) * s.HV];
+  ColTile<float, RT> tg[NCK];
+  ColTile<T, RT> tq[NCK], tk[NCK];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rt + 4 * grp + j;
-        G[rt][j] = row < len ? gc[row * gs + col] : 0.f;
-      }
-    col_prefix<RT>(G, lane);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rt + 4 * grp + j;
-        const int off = row * qs + col;
-        const float kv = row < len ? to_f(kc[off]) : 0.f;
-        const float qv = row < len ? to_f(qc[off]) : 0.f;
-        const float e = __expf(G[rt][j]);
-        Qd[row * LDK + col] = from_f<T>(s.scale * qv * e);
-        Kd[row * LDK + col] = from_f<T>(kv * e);
-        Ki[row * LDK + col] = from_f<T>(kv * __expf(-G[rt][j]));
-      }
+  for (int ci = 0; ci < NCK; ++ci) {
+    const int kt = min(wave + ci * NW, KT - 1);
+    tg[ci].load(gc, gs, 16 * kt, lane, len);
+    tq[ci].load(qc, qs, 16 * kt, lane, len);
+    tk[ci].load(kc, qs, 16 * kt, lane, len);
   }
-  const T* Sin = states + ch * K * V;
-  for (int vt = wave; vt < VT; vt += NW) {
-    const int col = 16 * vt + n;
+  // bf16 (BLK): piece i of this lane lies in 16 x 32 block b = wave + i NW of the matrix
+  // (blocks down the rows first): row 16(b % row tiles) + n, columns 32(b / row tiles) + 8grp
+  // .. +7. Otherwise piece i of thread tid covers VEC elements of a row (S_in: lanes on
+  // consecutive rows).
+  constexpr bool BLK = sizeof(T) == 2 && C % 32 == 0 && V % 32 == 0 && K % 16 == 0;
+  constexpr int NBS = KT * (V / 32), NBI = RT * (C / 32);
+  auto blk_rc = [&](int b, int rtiles, int& r, int& cc) {
+    r = 16 * (b % rtiles) + n;
+    cc = 32 * (b / rtiles) + 8 * grp;
+  };
+  constexpr int NSV = (K * V / VEC + NTH - 1) / NTH;
+  vecT sv[NSV];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      f32x4 s4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s4[j] = to_f(Sin[(16 * kt + 4 * grp + j) * V + col]);
-      st4(SinT + col * LDK + 16 * kt + 4 * grp, s4);
+  for (int i = 0; i < NSV; ++i) {
+    if constexpr (BLK) {
+      int r, cc;
+      blk_rc(min(wave + i * NW, NBS - 1), KT, r, cc);
+      sv[i] = *reinterpret_cast<const vecT*>(Sin + r * V + cc);
+    } else {
+      const int pid = min(tid + i * NTH, K * V / VEC - 1);
+      sv[i] = *reinterpret_cast<const vecT*>(Sin + (pid % K) * V + (pid / K) * VEC);
     }
   }
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int i = idx / C, j = idx % C;
-    const float val = (i < len && j < len) ? to_f(invp[ch * C * C + idx]) : (i == j ? 1.f : 0.f);
-    INVt[i * LDC + j] = from_f<T>(val);
+  constexpr int NIV = (C * C / VEC + NTH - 1) / NTH;
+  vecT iv[NIV];
+#pragma unroll
+  for (int i = 0; i < NIV; ++i) {
+    if constexpr (BLK) {
+      int r, cc;
+      blk_rc(min(wave + i * NW, NBI - 1), RT, r, cc);
+      iv[i] = *reinterpret_cast<const vecT*>(invc + r * C + cc);
+    } else {
+      iv[i] = *reinterpret_cast<const vecT*>(invc + min(tid + i * NTH, C * C / VEC - 1) * VEC);
+    }
+  }
+  // v at the places of the C x V accumulator tiles this wave owns in the block walk of the
+  // products below (RT x VT tiles in blocks of 1 x BN)
+  ColTile<T, 1> tv[NIT1][BN];
+#pragma unroll
+  for (int it = 0; it < NIT1; ++it) {
+    const int blk = min(wave + it * NW, RT * (VT / BN) - 1);
+    const int mt = blk / (VT / BN), nt0 = (blk % (VT / BN)) * BN;
+#pragma unroll
+    for (int jb = 0; jb < BN; ++jb) tv[it][jb].load(vc, vs, 16 * (nt0 + jb), lane, len, 16 * mt);
+  }
+  if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
+
+  // ---- gate cumsum; qd, kd, ki row-major; S_in^T; INV
+#pragma unroll
+  for (int ci = 0; ci < NCK; ++ci) {
+    const int kt = wave + ci * NW;
+    if (kt < KT) {
+      float G[RT][4], qv[RT][4], kv[RT][4];
+      tg[ci].get(G, lane, len);
+      tq[ci].get(qv, lane, len);
+      tk[ci].get(kv, lane, len);
+      col_prefix<RT>(G, lane);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 q4, kd4, ki4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e = __expf(G[rt][j]);
+          q4[j] = s.scale * qv[rt][j] * e;
+          kd4[j] = kv[rt][j] * e;
+          ki4[j] = kv[rt][j] * __expf(-G[rt][j]);
+        }
+        store_rows<T>(Qd, LDK, 16 * rt, 16 * kt, q4, lane, 1 << 30);
+        store_rows<T>(Kd, LDK, 16 * rt, 16 * kt, kd4, lane, 1 << 30);
+        store_rows<T>(Ki, LDK, 16 * rt, 16 * kt, ki4, lane, 1 << 30);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NSV; ++i) {
+    if constexpr (BLK) {
+      const int b = wave + i * NW;
+      if (b < NBS) store_T_block(SinT, LDK, 16 * (b % KT), 32 * (b / KT), sv[i], lane);
+    } else {
+      const int pid = tid + i * NTH;
+      if (pid < K * V / VEC) {
+        const int row = pid % K, c0 = (pid / K) * VEC;
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) SinT[(c0 + t) * LDK + row] = sv[i][t];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NIV; ++i) {
+    int r, c0;
+    bool ok;
+    if constexpr (BLK) {
+      const int b = wave + i * NW;
+      ok = b < NBI;
+      blk_rc(b, RT, r, c0);
+    } else {
+      const int pid = tid + i * NTH;
+      ok = pid < C * C / VEC;
+      r = (pid * VEC) / C;
+      c0 = (pid * VEC) % C;
+    }
+    if (ok) {
+      vecT m;
+#pragma unroll
+      for (int t = 0; t < VEC; ++t) m[t] = (r < len && c0 + t < len) ? iv[i][t] : from_f<T>(r == c0 + t ? 1.f : 0.f);
+      if constexpr (sizeof(T) == 2) {
+        st_2x8(INVt + r * LDC + c0, m);
+      } else {
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) INVt[r * LDC + c0 + t] = m[t];
+      }
+    }
+  }
+  t4 vraw[NIT1][BN];
+#pragma unroll
+  for (int it = 0; it < NIT1; ++it) {
+    const int blk = min(wave + it * NW, RT * (VT / BN) - 1);
+    const int mt = blk / (VT / BN);
+#pragma unroll
+    for (int jb = 0; jb < BN; ++jb) {
+      float x[1][4];
+      tv[it][jb].get(x, lane, len, 16 * mt);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vraw[it][jb][j] = from_f<T>(x[0][j]);
+    }
   }
   __syncthreads();
 
-  constexpr int BN = VT % 2 == 0 ? 2 : 1;
-  // vcorr = diag(beta)(v - kd S_in), stored transposed.
+  // ---- vcorr = diag(beta)(v - kd S_in), stored transposed; Mqk = tril(qd ki^T), row-major
   block_gemm<T, RT, VT, BN, NW, K>(Kd, LDK, 1 << 30, SinT, LDK, FullRange(),
-                                   [&](int, int mt, int nt0, f32x4(&acc)[BN]) {
+                                   [&](int it, int mt, int nt0, f32x4(&acc)[BN]) {
 #pragma unroll
                                      for (int jb = 0; jb < BN; ++jb) {
                                        const int col = 16 * (nt0 + jb) + n;
                                        f32x4 vc4;
 #pragma unroll
-                                       for (int j = 0; j < 4; ++j) {
-                                         const int row = 16 * mt + 4 * grp + j;
-                                         const float vv =
-                                             row < len ? to_f(vc[row * vs + col]) : 0.f;
-                                         vc4[j] = betas[row] * (vv - acc[jb][j]);
-                                       }
+                                       for (int j = 0; j < 4; ++j)
+                                         vc4[j] = betas[16 * mt + 4 * grp + j] * (to_f(vraw[it][jb][j]) - acc[jb][j]);
                                        st4(VcT + col * LDC + 16 * mt + 4 * grp, vc4);
                                      }
                                    }, wave, lane);
-  // Mqk = tril(qd ki^T), row-major.
   block_gemm<T, RT, RT, 1, NW, K>(
       Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
       [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+        f32x4 m4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
-          Mqk[row * LDC + col] = from_f<T>(col <= row ? acc[0][j] : 0.f);
-        }
+        for (int j = 0; j < 4; ++j) m4[j] = (16 * nt0 + n <= 16 * mt + 4 * grp + j) ? acc[0][j] : 0.f;
+        store_rows<T>(Mqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
       }, wave, lane);
   __syncthreads();
-  // U = INV vcorr, stored transposed.
+  // ---- U = INV vcorr, stored transposed
   block_gemm<T, RT, VT, BN, NW, C>(
       INVt, LDC, 1 << 30, VcT, LDC, [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
       [&](int, int mt, int nt0, f32x4(&acc)[BN]) {
@@ -333,18 +514,13 @@ __global__ __launch_bounds__(256) void fwd_out_kernel(Shape s, const T* __restri
         for (int jb = 0; jb < BN; ++jb) st4(UT + (16 * (nt0 + jb) + n) * LDC + 16 * mt + 4 * grp, acc[jb]);
       }, wave, lane);
   __syncthreads();
-  // o = qd S_in + Mqk U.
+  // ---- o = qd S_in + Mqk U, stored as row pieces
   block_gemm2<T, RT, VT, BN, NW, K, C>(
       Qd, LDK, SinT, LDK, FullRange(), Mqk, LDC, UT, LDC,
       [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
       [&](int, int mt, int nt0, f32x4(&acc)[BN]) {
 #pragma unroll
-        for (int jb = 0; jb < BN; ++jb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = 16 * mt + 4 * grp + j, col = 16 * (nt0 + jb) + n;
-            if (row < len) oc[row * vs + col] = from_f<T>(acc[jb][j]);
-          }
+        for (int jb = 0; jb < BN; ++jb) store_rows<T>(oc, vs, 16 * mt, 16 * (nt0 + jb), acc[jb], lane, len);
       }, wave, lane);
 }
 
@@ -357,7 +533,7 @@ template <class T, int K, int V, int C>
 static hipError_t fwd_prep_t(const Shape& s, const void* k, const void* v, const float* g, const float* beta,
                              void* inv, const FwdWs& ws, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_prep_kernel<T, K, V, C>), dim3(s.NT, s.nhv), dim3(256), 0, st, s,
+  hipLaunchKernelGGL((fwd_prep_kernel<T, K, V, C>), dim3(s.NT, s.nhv), dim3(512), 0, st, s,
                      static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<T*>(inv), ws);
   return hipGetLastError();
 }
@@ -373,7 +549,7 @@ template <class T, int K, int V, int C>
 static hipError_t fwd_out_t(const Shape& s, const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const void* states, const void* inv, void* o, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_out_kernel<T, K, V, C>), dim3(s.NT, s.nhv), dim3(256), 0, st, s,
+  hipLaunchKernelGGL((fwd_out_kernel<T, K, V, C>), dim3(s.NT, s.nhv), dim3(512), 0, st, s,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), g, beta,
                      static_cast<const T*>(states), static_cast<const T*>(inv), static_cast<T*>(o));
   return hipGetLastError();
