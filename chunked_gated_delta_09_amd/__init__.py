@@ -30,7 +30,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("HV", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("C", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("cu_seqlens_dev", ctypes.c_void_p), ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
-                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("beta_logits", ctypes.c_int32)]
 
 
 _lib = None
@@ -71,10 +71,12 @@ def _check(status):
         raise KdaError(status, load().kda_last_error().decode())
 
 
-def make_dims(B, T, H, HV, K, V, C, scale=None, dtype="bf16", cu_seqlens=None, cu_seqlens_dev=None):
+def make_dims(B, T, H, HV, K, V, C, scale=None, dtype="bf16", cu_seqlens=None, cu_seqlens_dev=None,
+              beta_logits=False):
     """Build a kda_dims. ``cu_seqlens`` (host list/tensor) selects packed sequences; the
     matching device copy must be passed as ``cu_seqlens_dev`` (int32 tensor on the GPU).
-    Returns (dims, keepalive)."""
+    ``beta_logits``: beta holds logits (sigmoid applied in the kernels, dbeta w.r.t. the
+    logits). Returns (dims, keepalive)."""
     dt = KDA_F32 if dtype in ("f32", "fp32", "float32") else KDA_BF16
     if scale is None:
         scale = 1.0 / math.sqrt(K)
@@ -83,9 +85,10 @@ def make_dims(B, T, H, HV, K, V, C, scale=None, dtype="bf16", cu_seqlens=None, c
         host = (ctypes.c_int32 * len(cu))(*cu)
         N = len(cu) - 1
         dev = ctypes.c_void_p(cu_seqlens_dev.data_ptr()) if cu_seqlens_dev is not None else None
-        d = Dims(B, T, H, HV, K, V, C, N, dev, ctypes.cast(host, ctypes.POINTER(ctypes.c_int32)), scale, dt)
+        d = Dims(B, T, H, HV, K, V, C, N, dev, ctypes.cast(host, ctypes.POINTER(ctypes.c_int32)), scale, dt,
+                 int(bool(beta_logits)))
         return d, (host, cu_seqlens_dev)
-    d = Dims(B, T, H, HV, K, V, C, B, None, None, scale, dt)
+    d = Dims(B, T, H, HV, K, V, C, B, None, None, scale, dt, int(bool(beta_logits)))
     return d, None
 
 
@@ -125,7 +128,7 @@ def _check_tensor(t, name, dtype, shape):
     del torch
 
 
-def _geometry(q_or_k, v, C, cu_seqlens, scale):
+def _geometry(q_or_k, v, C, cu_seqlens, scale, beta_logits=False):
     import torch
     B, T, H, K = q_or_k.shape
     HV, V = v.shape[2], v.shape[3]
@@ -135,16 +138,17 @@ def _geometry(q_or_k, v, C, cu_seqlens, scale):
         if B != 1:
             raise ValueError("packed sequences need batch size 1")
         cu_dev = torch.tensor([int(x) for x in cu_seqlens], dtype=torch.int32, device=q_or_k.device)
-    dims, keep = make_dims(B, T, H, HV, K, V, C, scale, dtype, cu_seqlens, cu_dev)
+    dims, keep = make_dims(B, T, H, HV, K, V, C, scale, dtype, cu_seqlens, cu_dev, beta_logits)
     return dims, keep, (B, T, H, HV, K, V, dims.N)
 
 
 def fwd_states(q, k, v, g, beta, h0=None, cu_seqlens=None, C=64, scale=None, output_o=False,
-               output_final_state=True):
+               output_final_state=True, beta_logits=False):
     """Forward chunk states. Returns dict(states [NT,HV,K,V], inv [NT,HV,C,C],
-    final_state [N,HV,K,V] fp32 or None, o [B,T,HV,V] or None)."""
+    final_state [N,HV,K,V] fp32 or None, o [B,T,HV,V] or None). ``beta_logits``: beta
+    holds logits (the kernels apply a sigmoid)."""
     import torch
-    dims, keep, (B, T, H, HV, K, V, N) = _geometry(k, v, C, cu_seqlens, scale)
+    dims, keep, (B, T, H, HV, K, V, N) = _geometry(k, v, C, cu_seqlens, scale, beta_logits)
     tdt = k.dtype
     for t, nm, sh in [(q, "q", (B, T, H, K)), (k, "k", (B, T, H, K)), (v, "v", (B, T, HV, V))]:
         _check_tensor(t, nm, tdt, sh)
@@ -178,11 +182,12 @@ def chunk_bwd_into(dims, q, k, v, g, beta, states, inv, dO, dS_final, dq, dk, dv
 
 
 def chunk_bwd(q, k, v, g, beta, states, inv, dO, dS_final=None, cu_seqlens=None, C=64, scale=None,
-              output_dh0=True):
+              output_dh0=True, beta_logits=False):
     """Chunkwise backward. Returns dict(dq, dk [B,T,H,K], dv [B,T,HV,V], dg [B,T,HV,K] fp32,
-    dbeta [B,T,HV] fp32, dh0 [N,HV,K,V] fp32 or None)."""
+    dbeta [B,T,HV] fp32, dh0 [N,HV,K,V] fp32 or None). ``beta_logits``: beta holds logits
+    and dbeta is the gradient w.r.t. them."""
     import torch
-    dims, keep, (B, T, H, HV, K, V, N) = _geometry(q, v, C, cu_seqlens, scale)
+    dims, keep, (B, T, H, HV, K, V, N) = _geometry(q, v, C, cu_seqlens, scale, beta_logits)
     tdt = q.dtype
     NT = num_chunks(dims)
     if NT < 0:

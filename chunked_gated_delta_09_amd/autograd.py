@@ -23,11 +23,11 @@ class KdaChunkFunction(torch.autograd.Function):
     precision in which the library takes dS_final."""
 
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, h0, cu_seqlens, C, scale, output_final_state):
+    def forward(ctx, q, k, v, g, beta, h0, cu_seqlens, C, scale, output_final_state, beta_logits):
         fw = fwd_states(q, k, v, g, beta, h0=h0, cu_seqlens=cu_seqlens, C=C, scale=scale, output_o=True,
-                        output_final_state=output_final_state)
+                        output_final_state=output_final_state, beta_logits=beta_logits)
         ctx.save_for_backward(q, k, v, g, beta, fw["states"], fw["inv"])
-        ctx.cu_seqlens, ctx.C, ctx.scale = cu_seqlens, C, scale
+        ctx.cu_seqlens, ctx.C, ctx.scale, ctx.beta_logits = cu_seqlens, C, scale, beta_logits
         ctx.h0_dtype = None if h0 is None else h0.dtype
         return fw["o"], fw["final_state"]
 
@@ -36,13 +36,16 @@ class KdaChunkFunction(torch.autograd.Function):
         q, k, v, g, beta, states, inv = ctx.saved_tensors
         dS = None if dfinal is None else dfinal.to(q.dtype).contiguous()
         r = chunk_bwd(q, k, v, g, beta, states, inv, do.to(q.dtype).contiguous(), dS_final=dS,
-                      cu_seqlens=ctx.cu_seqlens, C=ctx.C, scale=ctx.scale, output_dh0=ctx.h0_dtype is not None)
+                      cu_seqlens=ctx.cu_seqlens, C=ctx.C, scale=ctx.scale, output_dh0=ctx.h0_dtype is not None,
+                      beta_logits=ctx.beta_logits)
         dh0 = None if ctx.h0_dtype is None else r["dh0"].to(ctx.h0_dtype)
-        return r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], dh0, None, None, None, None
+        return r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], dh0, None, None, None, None, None
 
 
-def kda_chunk(q, k, v, g, beta, h0=None, cu_seqlens=None, C=64, scale=None, output_final_state=True):
+def kda_chunk(q, k, v, g, beta, h0=None, cu_seqlens=None, C=64, scale=None, output_final_state=True,
+              beta_logits=False):
     """Differentiable chunked KDA. Shapes: q, k [B,T,H,K]; v [B,T,HV,V]; g [B,T,HV,K] fp32;
-    beta [B,T,HV] fp32; h0 [N,HV,K,V] or None; packed sequences via cu_seqlens (host list,
-    B = 1). Returns (o [B,T,HV,V], S_T [N,HV,K,V] fp32 or None)."""
-    return KdaChunkFunction.apply(q, k, v, g, beta, h0, cu_seqlens, C, scale, output_final_state)
+    beta [B,T,HV] fp32 (write strengths, or their logits with ``beta_logits``); h0
+    [N,HV,K,V] or None; packed sequences via cu_seqlens (host list, B = 1). Returns
+    (o [B,T,HV,V], S_T [N,HV,K,V] fp32 or None)."""
+    return KdaChunkFunction.apply(q, k, v, g, beta, h0, cu_seqlens, C, scale, output_final_state, beta_logits)

@@ -60,6 +60,7 @@ kda_status validate(const kda_dims* d, Plan& p, bool launching) {
                 d->HV, d->K, d->V, d->C, d->N);
   if (d->HV % d->H != 0) return fail(KDA_EINVAL, "HV (%d) must be a multiple of H (%d)", d->HV, d->H);
   if (d->dtype != KDA_F32 && d->dtype != KDA_BF16) return fail(KDA_EINVAL, "unknown dtype %d", d->dtype);
+  if (d->beta_logits != 0 && d->beta_logits != 1) return fail(KDA_EINVAL, "beta_logits must be 0 or 1, got %d", d->beta_logits);
   if (!std::isfinite(d->scale)) return fail(KDA_EINVAL, "scale must be finite");
   const bool ok = (d->dtype == KDA_F32 && d->K == 16 && d->V == 16 && d->C == 16) ||
                   (d->dtype == KDA_BF16 && d->K == 128 && d->V == 128 && (d->C == 64 || d->C == 16));
@@ -153,6 +154,7 @@ kda::Shape make_shape(const kda_dims* d, const Plan& p, void* ws, size_t choff_o
   s.choff = p.varlen ? reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + choff_off) : nullptr;
   s.hv0 = 0;
   s.nhv = d->HV;
+  s.beta_logits = d->beta_logits;
   return s;
 }
 

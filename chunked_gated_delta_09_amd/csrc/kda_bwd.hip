@@ -95,7 +95,7 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
 
   KDA_TS(0, 0);
   // ---- every global load of the chunk, issued before any use
-  const float beta_raw = bc[min(tid % C, len - 1) * s.HV];
+  const float beta_raw = beta_of(bc[min(tid % C, len - 1) * s.HV], s.beta_logits);
   float G[NCK][RT][4], qv[NCK][RT][4], kv[NCK][RT][4], dov[NCV][RT][4];
 #pragma unroll
   for (int ci = 0; ci < NCK; ++ci) {
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     KDA_TS(2, 0);
     // ---- phase 1: every global load of this value head, issued before any use
     // beta: loaded with the rest, written to LDS once everything is in flight
-    const float beta_raw = bc[min(tid % C, len - 1) * s.HV];
+    const float beta_raw = beta_of(bc[min(tid % C, len - 1) * s.HV], s.beta_logits);
     for (int i = tid; i < NW * C; i += NTH) dbpart[i] = 0.f;  // dvc part (written sparsely)
     float Gr[NCT][RT][4], qv[NCT][RT][4], kv[NCT][RT][4];
     ColTile<float, RT> tg[NCT];
@@ -903,6 +903,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       for (int w = 0; w < NW; ++w) acc += dbpart[w * C + tid];
 #pragma unroll
       for (int w = 0; w < NW; ++w) acc += dbpart[NW * C + w * C + tid];
+      if (s.beta_logits) acc *= betas[tid] * (1.f - betas[tid]);  // d sigmoid / d logit
       dbc[tid * s.HV] = acc;
     }
     __syncthreads();

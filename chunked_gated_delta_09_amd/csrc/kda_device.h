@@ -75,6 +75,9 @@ __device__ __forceinline__ T from_f(float x) { return (T)x; }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// The write strength from the loaded beta value: itself, or the sigmoid of a logit.
+__device__ __forceinline__ float beta_of(float raw, int logits) { return logits ? 1.f / (1.f + __expf(-raw)) : raw; }
+
 // Padding (elements) added to the contiguous dimension of LDS matrices: 8 bytes, so a row
 // stride is an odd multiple of 8 bytes modulo 128. Measured on gfx950 (bank-conflict
 // counter): the 16 lanes of a lane group then hit distinct banks for 8-byte writes at 16

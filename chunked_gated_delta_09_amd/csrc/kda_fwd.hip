@@ -157,7 +157,7 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
 
   // ---- every global load, issued before any use (row pieces, moved to the column-owner
   // layout by the tiles' MFMA transposes)
-  const float beta_raw = bc[min(tid % C, len - 1) * s.HV];
+  const float beta_raw = beta_of(bc[min(tid % C, len - 1) * s.HV], s.beta_logits);
   ColTile<float, RT> tg[NCK];
   ColTile<T, RT> tk[NCK], tv[NCV];
 #pragma unroll
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
   const T* __restrict__ invc = invp + ch * C * C;
 
   // ---- loads
-  const float beta_raw = bc[min(tid % C, len - 1) * s.HV];
+  const float beta_raw = beta_of(bc[min(tid % C, len - 1) * s.HV], s.beta_logits);
   ColTile<float, RT> tg[NCK];
   ColTile<T, RT> tq[NCK], tk[NCK];
 #pragma unroll

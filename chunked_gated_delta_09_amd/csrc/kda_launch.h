@@ -16,6 +16,7 @@ struct Shape {
   const int32_t* cu;     // device cu_seqlens, or nullptr when dense
   const int32_t* choff;  // device first-chunk table [N+1], or nullptr when dense
   int hv0, nhv;          // value heads of this launch: hv0 .. hv0 + nhv - 1 (a multiple of HV / H)
+  int beta_logits;       // beta holds logits: kernels apply a sigmoid; dbeta is w.r.t. the logits
 };
 
 // Per-chunk workspace tensors of the forward (all [NT, HV, ...]).

@@ -68,6 +68,11 @@ typedef struct {
                                         are allowed.                                          */
     float scale;      /* output scale (1/sqrt(K) in the usual parameterisation)               */
     int32_t dtype;    /* kda_dtype                                                            */
+    int32_t beta_logits; /* 0: beta holds the write strengths in (0, 1). 1: beta holds their
+                            logits; every kernel takes beta = sigmoid(logit) (the FlashKDA
+                            backward page loads raw beta and applies a sigmoid), and
+                            kda_chunk_bwd's dbeta is the gradient w.r.t. the logits,
+                            dbeta * beta (1 - beta). Other values: KDA_EINVAL.              */
 } kda_dims;
 
 /* Total number of chunks NT = sum_n ceil(len_n / C); -1 if dims are invalid. */

@@ -68,11 +68,20 @@ def _f64(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
 
 
-def run(q, k, v, g, beta, cu_seqlens, scale, h0=None, dO=None, dS_final=None, backward=True, nthreads=0):
+def run(q, k, v, g, beta, cu_seqlens, scale, h0=None, dO=None, dS_final=None, backward=True, nthreads=0,
+        beta_logits=False):
     """Forward (o, S_T) and, if ``backward``, the VJP (dq, dk, dv, dg, dbeta, dh0) of
     L = sum_t <dO_t, o_t> + <dS_final, S_T>. Returns a dict of fp64 numpy arrays and the
-    number of threads used under key ``threads``."""
+    number of threads used under key ``threads``.
+
+    ``beta_logits``: ``beta`` holds logits x and the write strength is sigmoid(x) (the
+    FlashKDA backward page applies a sigmoid to the raw beta it loads); dbeta is then the
+    gradient w.r.t. x, the strength's gradient times sigmoid(x)(1 - sigmoid(x))."""
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    logit = None
+    if beta_logits:
+        logit = beta
+        beta = 1.0 / (1.0 + np.exp(-logit))
     h0, dO, dS_final = _f64(h0), _f64(dO), _f64(dS_final)
     T, H, K = q.shape
     HV, V = v.shape[1], v.shape[2]
@@ -93,6 +102,8 @@ def run(q, k, v, g, beta, cu_seqlens, scale, h0=None, dO=None, dS_final=None, ba
                             _ptr(out.get("dbeta")), _ptr(out.get("dh0")), int(nthreads))
     if nt < 0:
         raise ValueError("kda_oracle_run rejected its arguments")
+    if backward and beta_logits:
+        out["dbeta"] = out["dbeta"] * beta * (1.0 - beta)
     out["threads"] = nt
     return out
 

@@ -32,15 +32,15 @@ def to_dev(t):
     return None if t is None else t.contiguous().cuda()
 
 
-def run_gpu(inp, C=None, output_o=True):
+def run_gpu(inp, C=None, output_o=True, beta_logits=False):
     import chunked_gated_delta_09_amd as kda
     w = inp["workload"]
     C = w.C if C is None else C
     q, k, v, g, beta, h0, dsf, dO = (to_dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "h0", "dS_final", "dO"))
     f = kda.fwd_states(q, k, v, g, beta, h0=h0, cu_seqlens=inp["cu_seqlens"], C=C, scale=inp["scale"],
-                       output_o=output_o)
+                       output_o=output_o, beta_logits=beta_logits)
     b = kda.chunk_bwd(q, k, v, g, beta, f["states"], f["inv"], dO, dS_final=dsf, cu_seqlens=inp["cu_seqlens"], C=C,
-                      scale=inp["scale"])
+                      scale=inp["scale"], beta_logits=beta_logits)
     torch.cuda.synchronize()
     out = {key: (val.float().cpu().numpy() if val is not None else None) for key, val in {**f, **b}.items()}
     return out
@@ -60,7 +60,7 @@ def head_slices(inp, qk_heads=None):
     return list(qk_heads), v_heads
 
 
-def run_oracle(oracle_mod, inp, qk_heads=None):
+def run_oracle(oracle_mod, inp, qk_heads=None, beta_logits=False):
     """fp64 oracle on the given q/k heads (and their value heads), all sequences."""
     w = inp["workload"]
     qh, vh = head_slices(inp, qk_heads)
@@ -73,7 +73,7 @@ def run_oracle(oracle_mod, inp, qk_heads=None):
     dsf = None if inp["dS_final"] is None else _np(inp["dS_final"])[:, vh]
     cont = lambda a: None if a is None else np.ascontiguousarray(a)
     return oracle_mod.run(cont(q), cont(k), cont(v), cont(g), cont(beta), kin.flat_cu(inp), inp["scale"],
-                          h0=cont(h0), dO=cont(dO), dS_final=cont(dsf))
+                          h0=cont(h0), dO=cont(dO), dS_final=cont(dsf), beta_logits=beta_logits)
 
 
 def gpu_on_heads(inp, out, qk_heads=None):

@@ -70,6 +70,15 @@ def test_validation_errors(lib, kw, status, msg):
     assert kda.num_chunks(d) == -1 and kda.bwd_workspace_bytes(d) == 0
 
 
+def test_beta_logits_flag_validated(lib):
+    d, _ = _dims()
+    d.beta_logits = 2
+    assert _call_bwd(lib, d) == -1
+    assert "beta_logits" in lib.kda_last_error().decode()
+    d.beta_logits = 1
+    assert kda.num_chunks(d) > 0
+
+
 class _FakeDev:
     """Stands in for a device tensor: validation fails before the pointer is used."""
 

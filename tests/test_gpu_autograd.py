@@ -18,11 +18,15 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("name", list(CASES) + ["bf16_dense_logits"])
 def test_autograd_matches_oracle_and_direct_call(oracle_mod, name):
     from chunked_gated_delta_09_amd.autograd import kda_chunk
-    w, wid = CASES[name]
+    logits = name.endswith("_logits")
+    w, wid = CASES[name[:-len("_logits")] if logits else name]
     inp = kin.make_inputs(w, seed=91) if wid is None else kin.make_inputs(w, wid=wid)
+    if logits:
+        gen = torch.Generator().manual_seed(34)
+        inp["beta"] = 1.5 * torch.randn(inp["beta"].shape, generator=gen)
     if inp["dS_final"] is None:
         # the loss still needs a final-state term; a seeded one of the state's size
         gen = torch.Generator().manual_seed(5)
@@ -30,14 +34,14 @@ def test_autograd_matches_oracle_and_direct_call(oracle_mod, name):
     leaf = {n: inp[n].contiguous().cuda().requires_grad_(True) for n in ("q", "k", "v", "g", "beta")}
     h0 = None if inp["h0"] is None else inp["h0"].contiguous().cuda().requires_grad_(True)
     o, fin = kda_chunk(leaf["q"], leaf["k"], leaf["v"], leaf["g"], leaf["beta"], h0=h0, cu_seqlens=inp["cu_seqlens"],
-                       C=w.C, scale=inp["scale"])
+                       C=w.C, scale=inp["scale"], beta_logits=logits)
     dO = inp["dO"].cuda().float()
     dsf = inp["dS_final"].cuda().float()
     loss = (o.float() * dO).sum() + (fin * dsf).sum()
     loss.backward()
     torch.cuda.synchronize()
 
-    ref = run_oracle(oracle_mod, inp)
+    ref = run_oracle(oracle_mod, inp, beta_logits=logits)
     B, T = inp["B"], inp["T"]
     got = {
         "dq": leaf["q"].grad.float().cpu().numpy().reshape(B * T, w.H, w.K),
@@ -56,7 +60,7 @@ def test_autograd_matches_oracle_and_direct_call(oracle_mod, name):
     assert all(e <= tol for e in errs.values()), errs
 
     # the same kernels on the same inputs through the direct calls: identical gradients
-    direct = run_gpu(inp)
+    direct = run_gpu(inp, beta_logits=logits)
     for key in ("dq", "dk", "dv", "dg", "dbeta"):
         a = got[key].reshape(-1)
         b = direct[key].reshape(-1)

@@ -128,3 +128,17 @@ def test_full_workload_sampled_heads(oracle_mod, wid):
     errs, bad = compare(inp, out, ref, qk_heads=heads)
     _report(f"full w{wid}", errs)
     assert not bad, bad
+
+
+@pytest.mark.parametrize("name", ["dense_ragged", "varlen_edges", "w0_fp32"])
+def test_beta_logits(oracle_mod, name):
+    """beta given as logits (sigmoid in the kernels, dbeta w.r.t. the logits) against the
+    oracle in the same mode."""
+    inp = kin.make_inputs(kin.WORKLOADS[0], wid=0) if name == "w0_fp32" else _small_inputs(name)
+    gen = torch.Generator().manual_seed(33)
+    inp["beta"] = 1.5 * torch.randn(inp["beta"].shape, generator=gen)
+    out = run_gpu(inp, beta_logits=True)
+    ref = run_oracle(oracle_mod, inp, beta_logits=True)
+    errs, bad = compare(inp, out, ref)
+    _report(f"logits {name}", errs)
+    assert "dbeta" in errs and not bad, bad

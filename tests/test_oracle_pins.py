@@ -69,6 +69,40 @@ def test_finite_differences(oracle_mod, case):
         assert rel(ref[gname], fd) < 1e-7, (case, gname, rel(ref[gname], fd))
 
 
+def test_finite_differences_beta_logits(oracle_mod):
+    """With beta given as logits x (strength sigmoid(x)), dbeta is the derivative of the loss
+    w.r.t. x: central differences of the forward in x."""
+    rng = np.random.default_rng(21)
+    T, K, V = 7, 4, 4
+    cu = [0, 7]
+    x = rand_inputs(rng, T, 1, 2, K, V, 1)
+    x["beta"] = 1.5 * rng.standard_normal((T, 2))  # logits, both signs
+    scale = K ** -0.5
+
+    def runl(y, backward=True):
+        return oracle_mod.run(y["q"], y["k"], y["v"], y["g"], y["beta"], cu, scale, h0=y["h0"], dO=y["dO"],
+                              dS_final=y["dS_final"], backward=backward, beta_logits=True)
+
+    ref = runl(x)
+    eps = 1e-6
+    fd = np.zeros_like(x["beta"])
+    for idx in np.ndindex(x["beta"].shape):
+        y = dict(x)
+        y["beta"] = x["beta"].copy()
+        y["beta"][idx] += eps
+        lp = oracle_mod.loss(runl(y, False), x["dO"], x["dS_final"])
+        y["beta"][idx] -= 2 * eps
+        lm = oracle_mod.loss(runl(y, False), x["dO"], x["dS_final"])
+        fd[idx] = (lp - lm) / (2 * eps)
+    assert rel(ref["dbeta"], fd) < 1e-7, rel(ref["dbeta"], fd)
+    # the other gradients equal those of the strengths sigmoid(x) given directly
+    y = dict(x)
+    y["beta"] = 1.0 / (1.0 + np.exp(-x["beta"]))
+    direct = run(oracle_mod, y, cu, scale)
+    for gname in ("dq", "dk", "dv", "dg", "dh0"):
+        assert np.array_equal(ref[gname], direct[gname]), gname
+
+
 def test_hand_worked_scalar_example(oracle_mod):
     # K = V = 1, scale = 1, h0 = 1. Token 1: k=1, beta=0.5, g=ln 0.5, v=2, q=1.
     # Token 2: k=1, beta=0.25, g=0, v=-1, q=2. dO = (1, 1), no dS_final.
