@@ -164,16 +164,19 @@ __global__ __launch_bounds__(64) void scan_kernel(Shape s, const T* __restrict__
 //  - a touch wave keeps the operands TOUCH_AHEAD chunks further on moving into L2 (one
 //    4-byte load per 128-byte line into a scratch LDS word, never waited for until exit).
 // All waves meet at one barrier per chunk step. The compute waves read the fragments from
-// LDS (contiguous 16-byte reads per lane) and load their own slice's seed tiles (W or Z)
-// from global memory one step ahead into a register double buffer. Pulling the shared
-// operands once per workgroup instead of once per slice is what sets the step time: a CU
-// moves only ~50 GB/s from L2.
+// LDS (contiguous 16-byte reads per lane, issued well ahead of their MFMAs); their own
+// slice's seed tiles (W or Z) come through the ring too when a workgroup holds at most 4
+// slices, and otherwise from global memory one step ahead into a register double buffer.
+// The shared operands are pulled once per workgroup instead of once per slice (a CU moves
+// only ~50 GB/s from L2); with one slice per workgroup the compute wave's own dependency
+// chain (two MFMA products and the state update) then sets the step time.
 //
 // Backward direction: a column slice covers the columns ScanCols::col(vt, n) (not 16
 // consecutive ones), and the per-chunk dS leaves exactly as this wave holds it, 4 values
 // per lane and row tile in seed order (one 8-byte store per row tile); the gradient kernel
 // transposes it, and the column choice makes the transposed values of two slices one
 // contiguous B fragment.
+
 // Global -> LDS copies (lane i's bytes land at lds + i * bytes). Issued as inline assembly:
 // the compiler's wait insertion would otherwise treat every LDS read of the ring as
 // depending on these copies and make the reading wave wait for all of its own outstanding
