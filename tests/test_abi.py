@@ -119,3 +119,17 @@ def test_workload_table_is_consistent():
         else:
             assert w.B > 0 and w.T > 0
         assert w.HV % w.H == 0
+
+
+def test_entry_points_reject_host_tensors():
+    """The product path has no CPU fallback: host tensors are refused before any launch."""
+    import torch
+    from chunked_gated_delta_09_amd.autograd import kda_chunk
+    q = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
+    v = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
+    g = torch.zeros(1, 64, 1, 128)
+    beta = torch.zeros(1, 64, 1)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.fwd_states(q, q, v, g, beta)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda_chunk(q, q, v, g, beta)

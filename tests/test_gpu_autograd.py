@@ -65,3 +65,29 @@ def test_autograd_matches_oracle_and_direct_call(oracle_mod, name):
         a = got[key].reshape(-1)
         b = direct[key].reshape(-1)
         assert np.array_equal(a, b), key
+
+
+def test_autograd_without_final_state(oracle_mod):
+    """output_final_state=False: only o takes part in the loss (dS_final absent)."""
+    from chunked_gated_delta_09_amd.autograd import kda_chunk
+    w = small_workload("ag_nofinal", B=1, T=140, H=1, HV=2, has_h0=True, has_dsf=False)
+    inp = kin.make_inputs(w, seed=92)
+    leaf = {n: inp[n].contiguous().cuda().requires_grad_(True) for n in ("q", "k", "v", "g", "beta")}
+    h0 = inp["h0"].contiguous().cuda().requires_grad_(True)
+    o, fin = kda_chunk(leaf["q"], leaf["k"], leaf["v"], leaf["g"], leaf["beta"], h0=h0, C=w.C, scale=inp["scale"],
+                       output_final_state=False)
+    assert fin is None
+    (o.float() * inp["dO"].cuda().float()).sum().backward()
+    torch.cuda.synchronize()
+    ref = run_oracle(oracle_mod, inp)
+    B, T = inp["B"], inp["T"]
+    errs = {
+        "dq": rel_l2(leaf["q"].grad.float().cpu().numpy().reshape(B * T, w.H, w.K), ref["dq"]),
+        "dk": rel_l2(leaf["k"].grad.float().cpu().numpy().reshape(B * T, w.H, w.K), ref["dk"]),
+        "dv": rel_l2(leaf["v"].grad.float().cpu().numpy().reshape(B * T, w.HV, w.V), ref["dv"]),
+        "dg": rel_l2(leaf["g"].grad.cpu().numpy().reshape(B * T, w.HV, w.K), ref["dg"]),
+        "dbeta": rel_l2(leaf["beta"].grad.cpu().numpy().reshape(B * T, w.HV), ref["dbeta"]),
+        "dh0": rel_l2(h0.grad.float().cpu().numpy(), ref["dh0"]),
+    }
+    print("[autograd no_final] " + " ".join(f"{k}={v:.2e}" for k, v in sorted(errs.items())), flush=True)
+    assert all(e <= TOL[w.dtype] for e in errs.values()), errs
