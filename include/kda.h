@@ -92,7 +92,7 @@ size_t kda_bwd_workspace_bytes(const kda_dims* dims);
  *   k        [B,T,H,K]  dtype
  *   v        [B,T,HV,V] dtype
  *   g        [B,T,HV,K] fp32    per-token natural-log decay (g <= 0 in practice)
- *   beta     [B,T,HV]   fp32    write strength
+ *   beta     [B,T,HV]   fp32    write strength, or its logit when dims->beta_logits = 1
  *   h0       [N,HV,K,V] dtype   initial state, NULL = zero
  * outputs:
  *   states   [NT,HV,K,V] dtype  S_in of every chunk (the state entering the chunk), chunks
@@ -124,7 +124,8 @@ kda_status kda_fwd_states(const kda_dims* dims, const void* q, const void* k, co
  *   dq, dk   [B,T,H,K]  dtype   summed over the value heads of each group
  *   dv       [B,T,HV,V] dtype
  *   dg       [B,T,HV,K] fp32    gradient w.r.t. the per-token g
- *   dbeta    [B,T,HV]   fp32    gradient w.r.t. beta itself (not a logit)
+ *   dbeta    [B,T,HV]   fp32    gradient w.r.t. beta as given: the strength itself, or its
+ *                               logit when dims->beta_logits = 1
  *   dh0      [N,HV,K,V] fp32    gradient w.r.t. h0, NULL = not written
  */
 kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const void* k, const void* v,
