@@ -719,32 +719,46 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         }
       }
     }
-    // ---- dMqk = tril(dO U^T); dL = strict_tril(-dvc U^T)
-    block_gemm<T, RT, RT, 1, NW, V>(
-        DoR, LDV, 1 << 30, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
-        [&](int, int mt, int nt0, f32x4(&acc)[1]) {
-          f32x4 m4;
+    // ---- dMqk = tril(dO U^T); dL = strict_tril(-dvc U^T), in one pass over the 16 x 16
+    // tiles: the two products share the U fragments, and tiles above the diagonal load
+    // nothing (their zeros are still written: phase 3 reads whole 32-wide steps)
+    {
+      constexpr int NB = RT * RT, NITM = (NB + NW - 1) / NW, NKV2 = V / M::KS;
+#pragma unroll
+      for (int it = 0; it < NITM; ++it) {
+        const int blk = wave + it * NW;
+        if (blk < NB) {
+          const int mt = blk / RT, nt0 = blk % RT;
+          f32x4 am = zero4(), al = zero4();
+          if (nt0 <= mt) {
+            typename M::frag fo[NKV2], fn[NKV2], fu[NKV2];
+#pragma unroll
+            for (int k = 0; k < NKV2; ++k) {
+              fu[k] = frag_ld<T>(U, LDV, 16 * nt0, k * M::KS, lane);
+              fo[k] = frag_ld<T>(DoR, LDV, 16 * mt, k * M::KS, lane);
+              fn[k] = frag_ld<T>(Ndv, LDV, 16 * mt, k * M::KS, lane);
+            }
+#pragma unroll
+            for (int k = 0; k < NKV2; ++k) {
+              am = M::mma(fo[k], fu[k], am);
+              al = M::mma(fn[k], fu[k], al);
+            }
+          }
+          f32x4 m4, l4, b4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
-            m4[j] = col <= row ? acc[0][j] : 0.f;
+            m4[j] = col <= row ? am[j] : 0.f;
+            l4[j] = col < row ? al[j] : 0.f;
+            b4[j] = betas[row] * l4[j];
           }
           store_rows<T>(DMqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
           st4(DMqkT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, m4);
-        }, wave, lane);
-    block_gemm<T, RT, RT, 1, NW, V>(
-        Ndv, LDV, 1 << 30, U, LDV, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
-        [&](int it, int mt, int nt0, f32x4(&acc)[1]) {
-          f32x4 b4, l4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
-            l4[j] = col < row ? acc[0][j] : 0.f;
-            b4[j] = betas[row] * l4[j];
-          }
           store_rows<T>(DL, LDC, 16 * mt, 16 * nt0, l4, lane, 1 << 30);
           st4(BDLT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, b4);
-        }, wave, lane);
+        }
+      }
+    }
     __syncthreads();
 
     KDA_TS(2, 6);
