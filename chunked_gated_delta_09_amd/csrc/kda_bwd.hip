@@ -394,6 +394,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       c = 32 * (b / rtiles) + 8 * grp;
     };
     constexpr int NSV = (K * V / VEC + NTH - 1) / NTH;
+    // with one column tile per wave, the row pieces of S_in this wave loads here (blocks
+    // wave + i NW: rows 16 wave + n, columns 32 i + 8 grp) are the B fragments of its phase-3
+    // products, kept in registers instead of loading S_in a second time (not with grouped
+    // value heads, whose per-group accumulators leave no room for them)
+    constexpr bool SIN_REUSE = !GVA && BLK && NCT == 1 && KT == NW && NSV == V / M::KS;
     vecT sv[NSV];
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
@@ -709,7 +714,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       const int kt = min(wave + ci * NW, KT - 1);
 #pragma unroll
       for (int kk = 0; kk < NKV; ++kk) {
-        bs[ci][kk] = frag_ld16<T>(Sin, V, 16 * kt, kk * M::KS, lane);
+        // bf16: phase 1 loaded exactly these pieces (rows 16 wave + n, columns 32 kk + 8 grp)
+        if constexpr (SIN_REUSE) bs[ci][kk] = sv[kk];
+        else bs[ci][kk] = frag_ld16<T>(Sin, V, 16 * kt, kk * M::KS, lane);
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int b = 0; b < 2; ++b)
