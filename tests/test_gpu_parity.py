@@ -142,3 +142,21 @@ def test_beta_logits(oracle_mod, name):
     errs, bad = compare(inp, out, ref)
     _report(f"logits {name}", errs)
     assert "dbeta" in errs and not bad, bad
+
+
+def test_strong_decay_c16(oracle_mod):
+    """Per-token gates in [-5, -0.5] (a chunk of 64 tokens would sum to about -175, beyond the
+    fp32 range of the factorised e^{+-G}); with C = 16 every chunk-local cumsum stays above -80,
+    so the kernels' e^{-G} stays below ~6e34, and the result matches the oracle."""
+    w = small_workload("strong_decay", B=2, T=100, H=2, HV=4, C=16, has_h0=True, has_dsf=True)
+    inp = kin.make_inputs(w, seed=21)
+    gen = torch.Generator().manual_seed(22)
+    inp["g"] = -(0.5 + 4.5 * torch.rand(inp["g"].shape, generator=gen))
+    assert float(inp["g"].min()) >= -5.0
+    out = run_gpu(inp)
+    for key in GRADS:
+        assert np.isfinite(out[key]).all(), key
+    ref = run_oracle(oracle_mod, inp)
+    errs, bad = compare(inp, out, ref)
+    _report("strong decay C=16", errs)
+    assert not bad, bad
