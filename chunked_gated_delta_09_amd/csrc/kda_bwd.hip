@@ -269,7 +269,9 @@ struct GradLds {
   static constexpr size_t oBeta = oMqkT + szCC;
   static constexpr size_t oDbp = oBeta + sizeof(float) * C;
   static constexpr size_t oDoT = oDbp + sizeof(float) * 2 * NW * C;  // dbeta partials: dvc part, then phase-3 part
-  static constexpr size_t total = oDoT + szVC;
+  // dg leaves through the dO slot in passes of SR rows of K fp32 (row stride K + 4)
+  static constexpr int SR = C < 32 ? C : 32;
+  static constexpr size_t total = mx(oDoT + szVC, oDoT + sizeof(float) * SR * (K + 4));
   static_assert(total <= 160 * 1024, "gradient kernel exceeds the LDS of one CU");
 };
 
@@ -876,21 +878,32 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
           for (int j = 0; j < 4; ++j) dGk[ci][rt][j] = dG[rt][j];
       }
     }
-    // dg leaves as 16-byte row pieces: each 16 x 16 fp32 tile moves from the column-owner
-    // layout to the row layout by four fp32 MFMAs against 0/1 selectors (exact: one nonzero
-    // product per output); this lane then holds row 16rt + n, columns 16kt + 4grp .. +3
+    // dg leaves through LDS (the dO slot, dead after the products above) as whole rows:
+    // 16-byte stores, consecutive lanes on consecutive columns.
+    {
+      constexpr int SR = Lay::SR;  // rows per pass
+      constexpr int LDG = K + 4;
+      float* stg = reinterpret_cast<float*>(smem + Lay::oDoT);
 #pragma unroll
-    for (int ci = 0; ci < NCT; ++ci) {
-      const int kt = wave + ci * NW;
-      if (kt < KT) {
+      for (int pass = 0; pass < C / SR; ++pass) {
+        __syncthreads();
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          f32x4 d = zero4();
+        for (int ci = 0; ci < NCT; ++ci) {
+          const int kt = wave + ci * NW;
+          if (kt < KT) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            d = __builtin_amdgcn_mfma_f32_16x16x4f32(dGk[ci][rt][j], n == 4 * grp + j ? 1.f : 0.f, d, 0, 0, 0);
-          const int row = 16 * rt + n;
-          if (row < len) *reinterpret_cast<f32x4*>(dgc + row * gs + 16 * kt + 4 * grp) = d;
+            for (int rt = 0; rt < RT; ++rt)
+              if (rt * 16 >= pass * SR && rt * 16 < (pass + 1) * SR) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) stg[(16 * rt + 4 * grp + j - pass * SR) * LDG + 16 * kt + n] = dGk[ci][rt][j];
+              }
+          }
+        }
+        __syncthreads();
+        for (int i = tid; i < SR * K / 4; i += NTH) {
+          const int r = i / (K / 4), c4 = (i % (K / 4)) * 4;
+          const int row = pass * SR + r;
+          if (row < len) *reinterpret_cast<f32x4*>(dgc + row * gs + c4) = *reinterpret_cast<const f32x4*>(stg + r * LDG + c4);
         }
       }
     }
