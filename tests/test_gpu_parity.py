@@ -36,6 +36,9 @@ SMALL = {
                                    has_h0=True, has_dsf=True),
     "c16": small_workload("c16", B=1, T=90, H=2, HV=2, C=16, has_h0=True, has_dsf=True),
     "single_partial_chunk": small_workload("single_partial_chunk", B=3, T=37, H=1, HV=2, has_dsf=True),
+    "gva3_varlen": small_workload("gva3_varlen", H=2, HV=6, varlen=3, total=300, len_lo=20, len_hi=200,
+                                  has_h0=True, has_dsf=True),
+    "gva8": small_workload("gva8", B=1, T=96, H=1, HV=8, has_h0=False, has_dsf=True),
 }
 
 
