@@ -67,8 +67,8 @@ def algorithmic_bytes(w, inp):
 
 
 def algorithmic_flops(w, inp):
-    """14 K V + 10 C K flop per token-head (seven C x K x V products and ten C x C x D
-    triangle products per chunk, counted dense)."""
+    """14 K V + 10 C K flop per token-head: seven C x K x V products and ten triangular
+    C x C x D products per chunk (C^2 D / 2 multiply-adds each), at 2 flop per multiply-add."""
     return (14 * w.K * w.V + 10 * w.C * w.K) * inp["B"] * inp["T"] * w.HV
 
 

@@ -1,0 +1,69 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard and the roofline accounting."""
+import importlib.util
+import math
+import os
+import subprocess
+import sys
+
+from chunked_gated_delta_09_amd import inputs as kin
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "single MI355X" in r.stderr
+
+
+def _per_token_head_bytes(K, V, C, es, group):
+    """Bytes per token-head counted from the operation's inputs and outputs: q, k and their
+    gradients are shared by the `group` value heads of a q/k head; g, dg are fp32 per channel;
+    beta, dbeta fp32 per token; the chunk's state S_in (K x V) and inverse (C x C) are spread
+    over its C tokens."""
+    reads = (2 * K * es) / group + 2 * V * es + 4 * K + 4 + (K * V + C * C) * es / C
+    writes = (2 * K * es) / group + V * es + 4 * K + 4
+    return reads + writes
+
+
+def test_algorithmic_bytes_match_the_per_token_head_count():
+    bench = _bench()
+    for wid in (1, 2, 4):
+        w = kin.WORKLOADS[wid]
+        inp = kin.make_inputs(w, wid=wid)
+        th = inp["B"] * inp["T"] * w.HV
+        per_seq = w.HV * w.K * w.V * (4 + (2 if inp["dS_final"] is not None else 0))  # dh0 fp32, dS_final bf16
+        expect = th * _per_token_head_bytes(w.K, w.V, w.C, 2, w.HV // w.H) + inp["N"] * per_seq
+        assert bench.algorithmic_bytes(w, inp) == round(expect), wid
+    # the figure quoted for the bench workload (B=2, T=2048, H=8): 3,464 B per token-head
+    w1 = kin.WORKLOADS[1]
+    assert _per_token_head_bytes(w1.K, w1.V, w1.C, 2, 1) == 3464
+    assert bench.algorithmic_bytes(w1, kin.make_inputs(w1, wid=1)) == 115_081_216
+
+
+def test_algorithmic_flops_count():
+    bench = _bench()
+    w = kin.WORKLOADS[1]
+    inp = kin.make_inputs(w, wid=1)
+    # seven C x K x V products and ten triangular C x C x D products (C^2 D / 2 MACs each) per
+    # chunk, 2 flop per MAC
+    per_chunk = 2 * 7 * w.C * w.K * w.V + 10 * w.C * w.C * w.K
+    chunks = inp["B"] * math.ceil(inp["T"] / w.C) * w.HV
+    assert bench.algorithmic_flops(w, inp) == per_chunk * chunks
+
+
+def test_recorded_traffic_follows_the_sources():
+    bench = _bench()
+    w = kin.WORKLOADS[1]
+    t = bench.recorded_traffic(w.name)
+    # either the record matches the current sources (a positive byte count) or it is withheld
+    assert t is None or t > bench.algorithmic_bytes(w, kin.make_inputs(w, wid=1))
+    assert bench.recorded_traffic("no_such_workload") is None
