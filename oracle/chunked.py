@@ -26,6 +26,13 @@ Backward, given dO and dS (gradient w.r.t. S_out):
   dg = reverse cumsum of dG within the chunk
 
 Plain numpy; no blocking beyond the chunking the method itself defines.
+
+``bf16_operands=True`` is an error model of a bf16 implementation, not a definition: every
+operand of a matrix product above, every per-chunk tensor kept between the passes (S_in,
+INV, the state gradient of each chunk) and the outputs dq, dk, dv are rounded to bf16
+(round to nearest even); products, sums and the elementwise gate algebra stay in fp64 (the
+FlashKDA backward page keeps its workspace in bf16 and does its math in fp32). Its
+per-tensor error against the fp64 definition predicts the error a bf16 kernel can expect.
 """
 from __future__ import annotations
 
@@ -51,10 +58,19 @@ def chunk_table(cu_seqlens, C):
     return out
 
 
-def chunked_fwd_bwd(q, k, v, g, beta, cu_seqlens, scale, C, h0=None, dO=None, dS_final=None, backward=True):
+def _bf16(a):
+    """Round to the nearest bf16 value (ties to even), returned as fp64."""
+    import torch
+    return torch.from_numpy(np.asarray(a, dtype=np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def chunked_fwd_bwd(q, k, v, g, beta, cu_seqlens, scale, C, h0=None, dO=None, dS_final=None, backward=True,
+                    bf16_operands=False):
     """Returns o, S_T and (if backward) dq, dk, dv, dg, dbeta, dh0, plus the per-chunk
     intermediates ``states`` (S_in, [NT, HV, K, V]), ``dstates`` (gradient w.r.t. each
-    chunk's S_out, [NT, HV, K, V]) and ``inv`` ([NT, HV, C, C], identity on padded rows)."""
+    chunk's S_out, [NT, HV, K, V]) and ``inv`` ([NT, HV, C, C], identity on padded rows).
+    ``bf16_operands``: the bf16 error model described in the module docstring."""
+    r = _bf16 if bf16_operands else (lambda a: a)
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     h0, dO, dS_final = _f64(h0), _f64(dO), _f64(dS_final)
     T, H, K = q.shape
@@ -97,17 +113,18 @@ def chunked_fwd_bwd(q, k, v, g, beta, cu_seqlens, scale, C, h0=None, dO=None, dS
                 kd = kc * np.exp(G)
                 ki = kc * np.exp(-G)
                 kr = kc * np.exp(gam[None, :] - G)
-                Lm = np.tril(b[:, None] * (kd @ ki.T), -1)
-                INV = np.linalg.inv(np.eye(L) + Lm)
-                Mqk = np.tril(qd @ ki.T)
-                vc0 = vc - kd @ S
-                U = INV @ (b[:, None] * vc0)
-                o[sl, h] = qd @ S + Mqk @ U
-                states[c, h] = S
+                Lm = np.tril(b[:, None] * (r(kd) @ r(ki).T), -1)
+                INV = r(np.linalg.inv(np.eye(L) + Lm))
+                Mqk = np.tril(r(qd) @ r(ki).T)
+                S_in = r(S)
+                vc0 = vc - r(kd) @ S_in
+                U = INV @ r(b[:, None] * vc0)
+                o[sl, h] = r(qd) @ S_in + r(Mqk) @ r(U)
+                states[c, h] = S_in
                 inv[c, h] = np.eye(C)
                 inv[c, h, :L, :L] = INV
-                saved.append((c, sl, L, qc, kc, b, G, gam, qd, kd, ki, kr, INV, Mqk, vc0, U, S.copy()))
-                S = np.exp(gam)[:, None] * S + kr.T @ U
+                saved.append((c, sl, L, qc, kc, b, G, gam, qd, kd, ki, kr, INV, Mqk, vc0, U, S_in))
+                S = np.exp(gam)[:, None] * S + r(kr).T @ r(U)
             S_T[n, h] = S
             if not backward:
                 continue
@@ -115,27 +132,28 @@ def chunked_fwd_bwd(q, k, v, g, beta, cu_seqlens, scale, C, h0=None, dO=None, dS
             for (c, sl, L, qc, kc, b, G, gam, qd, kd, ki, kr, INV, Mqk, vc0, U, S_in) in reversed(saved):
                 dstates[c, h] = dS
                 dOc = dO[sl, h]
-                dU = Mqk.T @ dOc + kr @ dS
-                dvc = INV.T @ dU
+                dSr = r(dS)
+                dU = r(Mqk).T @ dOc + r(kr) @ dSr
+                dvc = INV.T @ r(dU)
                 dv[sl, h] = b[:, None] * dvc
-                dS_in = np.exp(gam)[:, None] * dS + qd.T @ dOc - kd.T @ (b[:, None] * dvc)
-                dMqk = np.tril(dOc @ U.T)
-                dL = -np.tril(dvc @ U.T, -1)
-                dLki = dL @ ki
-                dqd = dOc @ S_in.T + dMqk @ ki
-                dkd = -b[:, None] * (dvc @ S_in.T) + b[:, None] * dLki
-                dki = dMqk.T @ qd + (b[:, None] * dL).T @ kd
-                dkr = U @ dS.T
+                dS_in = np.exp(gam)[:, None] * dS + r(qd).T @ dOc - r(kd).T @ r(b[:, None] * dvc)
+                dMqk = np.tril(dOc @ r(U).T)
+                dL = -np.tril(r(dvc) @ r(U).T, -1)
+                dLki = r(dL) @ r(ki)
+                dqd = dOc @ S_in.T + r(dMqk) @ r(ki)
+                dkd = -b[:, None] * (r(dvc) @ S_in.T) + b[:, None] * dLki
+                dki = r(dMqk).T @ r(qd) + r(b[:, None] * dL).T @ r(kd)
+                dkr = r(U) @ dSr.T
                 dbeta[sl, h] = np.sum(dvc * vc0, axis=1) + np.sum(kd * dLki, axis=1)
                 dq_h[sl, h] = scale * np.exp(G) * dqd
                 dk_h[sl, h] = np.exp(G) * dkd + np.exp(-G) * dki + np.exp(gam[None, :] - G) * dkr
                 dG = qd * dqd + kd * dkd - ki * dki - kr * dkr
-                dG[L - 1] += np.exp(gam) * np.sum(dS * S_in, axis=1) + np.sum(kr * dkr, axis=0)
+                dG[L - 1] += np.exp(gam) * np.sum(dSr * S_in, axis=1) + np.sum(kr * dkr, axis=0)
                 dg[sl, h] = np.cumsum(dG[::-1], axis=0)[::-1]
                 dS = dS_in
             dh0[n, h] = dS
     res.update(o=o, S_T=S_T, states=states, inv=inv)
     if backward:
-        res.update(dq=dq_h.reshape(T, H, Gs, K).sum(axis=2), dk=dk_h.reshape(T, H, Gs, K).sum(axis=2),
-                   dv=dv, dg=dg, dbeta=dbeta, dh0=dh0, dstates=dstates)
+        res.update(dq=r(dq_h.reshape(T, H, Gs, K).sum(axis=2)), dk=r(dk_h.reshape(T, H, Gs, K).sum(axis=2)),
+                   dv=r(dv), dg=dg, dbeta=dbeta, dh0=dh0, dstates=dstates)
     return res

@@ -163,3 +163,25 @@ def test_strong_decay_c16(oracle_mod):
     errs, bad = compare(inp, out, ref)
     _report("strong decay C=16", errs)
     assert not bad, bad
+
+
+@pytest.mark.parametrize("name", ["dense_ragged", "gva_ragged"])
+def test_error_matches_bf16_model(oracle_mod, name):
+    """The kernels lose no more precision than a bf16 implementation should: each gradient's
+    error against the oracle is within twice (plus 1e-3) what the chunked reference predicts
+    when every product operand and kept tensor is rounded to bf16."""
+    from oracle.chunked import chunked_fwd_bwd
+    inp = _small_inputs(name)
+    out = run_gpu(inp)
+    ref = run_oracle(oracle_mod, inp)
+    B, T = inp["B"], inp["T"]
+    f = lambda t: t.float().numpy().astype(np.float64).reshape(B * T, *t.shape[2:])
+    model = chunked_fwd_bwd(f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["g"]), f(inp["beta"]).reshape(B * T, -1),
+                            kin.flat_cu(inp), inp["scale"], 64, h0=inp["h0"].double().numpy(), dO=f(inp["dO"]),
+                            dS_final=inp["dS_final"].double().numpy(), bf16_operands=True)
+    errs, bad = compare(inp, out, ref)
+    assert not bad, bad
+    for key in GRADS:
+        predicted = rel_l2(model[key], ref[key])
+        print(f"[bf16 model {name}] {key}: gpu {errs[key]:.2e} model {predicted:.2e}", flush=True)
+        assert errs[key] <= 2 * predicted + 1e-3, (key, errs[key], predicted)

@@ -290,3 +290,26 @@ def test_thread_count_does_not_change_bits(oracle_mod):
                        dS_final=x["dS_final"], nthreads=4)
     for key in ["o", "S_T"] + GRADS:
         assert np.array_equal(a[key], b[key]), key
+
+
+def test_bf16_error_model_within_budget(oracle_mod):
+    """The chunked reference with every product operand and kept tensor rounded to bf16 (an
+    error model, not a definition) stays inside the 2e-2 per-tensor budget on a bf16 case with
+    ragged chunks, and its rounding is live (errors well above fp64 noise)."""
+    from chunked_gated_delta_09_amd import inputs as kin
+    from oracle.chunked import chunked_fwd_bwd
+    from tests.kda_cases import GRADS, rel_l2, run_oracle, small_workload
+    w = small_workload("budget", B=2, T=150, H=2, HV=2, has_h0=True, has_dsf=True)
+    inp = kin.make_inputs(w, seed=77)
+    ref = run_oracle(oracle_mod, inp)
+    B, T = inp["B"], inp["T"]
+    f = lambda t: t.float().numpy().astype(np.float64).reshape(B * T, *t.shape[2:])
+    args = (f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["g"]), f(inp["beta"]).reshape(B * T, -1), kin.flat_cu(inp),
+            inp["scale"], 64)
+    kw = dict(h0=inp["h0"].double().numpy(), dO=f(inp["dO"]), dS_final=inp["dS_final"].double().numpy())
+    exact = chunked_fwd_bwd(*args, **kw)
+    model = chunked_fwd_bwd(*args, bf16_operands=True, **kw)
+    for key in GRADS + ["o"]:
+        assert rel_l2(exact[key], ref[key]) < 1e-10, key
+        e = rel_l2(model[key], ref[key])
+        assert 1e-4 < e < 2e-2, (key, e)
