@@ -1,0 +1,89 @@
+"""GPU invariants of the library that need no oracle: the backward is linear in its
+cotangents (dO, dS_final); packed sequences equal separate runs; grouped value heads equal
+the heads expanded with q and k replicated, then summed over each group. Each runs on the
+fp32 path (K = V = C = 16, tight tolerances) and the bf16 path (K = V = 128, C = 64,
+tolerances at bf16 rounding level)."""
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_delta_09_amd import inputs as kin
+from tests.kda_cases import GRADS, rel_l2, run_gpu, small_workload
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {
+    "f32": (dict(K=16, V=16, C=16, dtype="f32"), 1e-5),
+    "bf16": (dict(K=128, V=128, C=64, dtype="bf16"), 2e-2),
+}
+
+
+def _wl(name, path, **kw):
+    dims, _ = PATHS[path]
+    return small_workload(name, **{**dims, **kw})
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_linear_in_cotangents(path):
+    tol = PATHS[path][1]
+    inp = kin.make_inputs(_wl("lin", path, B=2, T=90, H=1, HV=2, has_h0=True, has_dsf=True), seed=11)
+    gen = torch.Generator().manual_seed(12)
+    dO2 = torch.randn(inp["dO"].shape, generator=gen).to(inp["dO"].dtype)
+    dsf2 = (0.1 * torch.randn(inp["dS_final"].shape, generator=gen)).to(inp["dS_final"].dtype)
+    a = run_gpu(inp, output_o=False)
+    b = run_gpu({**inp, "dO": dO2, "dS_final": dsf2}, output_o=False)
+    # 2 dO1 - dO2 is exact in bf16 only up to rounding; take it from the fp32 sum
+    mix = {**inp, "dO": (2 * inp["dO"].float() - dO2.float()).to(inp["dO"].dtype),
+           "dS_final": (2 * inp["dS_final"].float() - dsf2.float()).to(inp["dS_final"].dtype)}
+    c = run_gpu(mix, output_o=False)
+    for key in GRADS:
+        e = rel_l2(c[key], 2 * a[key].astype(np.float64) - b[key])
+        print(f"[linear {path}] {key} {e:.2e}", flush=True)
+        assert e < tol, (key, e)
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_packed_equals_separate_runs(path):
+    lens = [37, 70, 19] if path == "f32" else [150, 64, 97]
+    cu = [0]
+    for ln in lens:
+        cu.append(cu[-1] + ln)
+    w = _wl("packed", path, varlen=len(lens), total=cu[-1], len_lo=1, len_hi=max(lens), H=1, HV=2, has_h0=True,
+            has_dsf=True)
+    inp = kin.make_inputs(w, seed=13)
+    inp["cu_seqlens"] = cu
+    packed = run_gpu(inp)
+    for n, (s0, s1) in enumerate(zip(cu[:-1], cu[1:])):
+        one = {**inp, "B": 1, "T": s1 - s0, "N": 1, "cu_seqlens": None,
+               "workload": _wl("one", path, B=1, T=s1 - s0, H=1, HV=2, has_h0=True, has_dsf=True)}
+        for key in ("q", "k", "v", "g", "beta", "dO"):
+            one[key] = inp[key][:, s0:s1].contiguous()
+        for key in ("h0", "dS_final"):
+            one[key] = inp[key][n:n + 1].contiguous()
+        sep = run_gpu(one)
+        for key in ("dq", "dk", "dv", "dg", "dbeta", "o"):
+            e = rel_l2(packed[key][:, s0:s1], sep[key])
+            assert e < 1e-6, (n, key, e)
+        for key in ("dh0", "final_state"):
+            e = rel_l2(packed[key][n:n + 1], sep[key])
+            assert e < 1e-6, (n, key, e)
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_grouped_heads_equal_expanded_heads(path):
+    tol = PATHS[path][1]
+    G = 3
+    inp = kin.make_inputs(_wl("gva", path, B=1, T=80, H=1, HV=G, has_h0=True, has_dsf=True), seed=14)
+    grouped = run_gpu(inp)
+    exp = {**inp, "workload": _wl("exp", path, B=1, T=80, H=G, HV=G, has_h0=True, has_dsf=True)}
+    exp["q"] = inp["q"].repeat(1, 1, G, 1).contiguous()
+    exp["k"] = inp["k"].repeat(1, 1, G, 1).contiguous()
+    expanded = run_gpu(exp)
+    for key in ("dv", "dg", "dbeta", "dh0", "o", "final_state"):
+        e = rel_l2(grouped[key], expanded[key])
+        assert e < (1e-6 if key in ("o", "final_state") else tol), (key, e)
+    for key in ("dq", "dk"):
+        summed = expanded[key].astype(np.float64).sum(axis=2, keepdims=True)
+        e = rel_l2(grouped[key], summed)
+        print(f"[gva {path}] {key} {e:.2e}", flush=True)
+        assert e < tol, (key, e)
