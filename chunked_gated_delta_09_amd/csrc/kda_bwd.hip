@@ -76,7 +76,8 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
   T* QpT = reinterpret_cast<T*>(smem + Lay::oQpT);
   float* betas = reinterpret_cast<float*>(smem + Lay::oBeta);
 
-  const int c = blockIdx.x, h = s.hv0 + blockIdx.y;
+  // heads of one chunk are neighbouring workgroups: together they read whole token rows
+  const int c = blockIdx.x / s.nhv, h = s.hv0 + blockIdx.x % s.nhv;
   const int hq = h / (s.HV / s.H);
   const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, grp = lane >> 4;
@@ -324,7 +325,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
   T* DoT = reinterpret_cast<T*>(smem + Lay::oDoT);  // dO^T, then dO row-major (same slot)
   T* DoR = DoT;
 
-  const int c = blockIdx.x, hq = s.hv0 / (s.HV / s.H) + blockIdx.y;
+  // heads of one chunk are neighbouring workgroups: together they read whole token rows
+  const int nhq = s.nhv / (s.HV / s.H);
+  const int c = blockIdx.x / nhq, hq = s.hv0 / (s.HV / s.H) + blockIdx.x % nhq;
   const int Gq = s.HV / s.H;
   const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
   if (geo.len <= 0) return;
@@ -955,7 +958,7 @@ template <class T, int K, int V, int C>
 static hipError_t bwd_prep_t(const Shape& s, const void* q, const void* k, const float* g, const float* beta,
                              const void* inv, const void* dO, const BwdWs& ws, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C>), dim3(s.NT, s.nhv), dim3(64 * BwdPrepLds<T, K, V, C>::NW), 0, st, s,
+  hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C>), dim3(s.NT * s.nhv), dim3(64 * BwdPrepLds<T, K, V, C>::NW), 0, st, s,
                      static_cast<const T*>(q), static_cast<const T*>(k), g, beta, static_cast<const T*>(inv),
                      static_cast<const T*>(dO), ws);
   return hipGetLastError();
@@ -973,7 +976,7 @@ static hipError_t bwd_grad_t(const Shape& s, const void* q, const void* k, const
                              const float* beta, const void* states, const void* inv, const void* dO, const BwdWs& ws,
                              void* dq, void* dk, void* dv, float* dg, float* dbeta, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  const dim3 grid(s.NT, s.nhv / (s.HV / s.H)), block(64 * GradLds<T, K, V, C>::NW);
+  const dim3 grid(s.NT * (s.nhv / (s.HV / s.H))), block(64 * GradLds<T, K, V, C>::NW);
   if (s.HV > s.H) {
     hipLaunchKernelGGL((bwd_grad_kernel<T, K, V, C, true>), grid, block, 0, st, s, static_cast<const T*>(q),
                        static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<const T*>(states),
