@@ -185,3 +185,19 @@ def test_error_matches_bf16_model(oracle_mod, name):
         predicted = rel_l2(model[key], ref[key])
         print(f"[bf16 model {name}] {key}: gpu {errs[key]:.2e} model {predicted:.2e}", flush=True)
         assert errs[key] <= 2 * predicted + 1e-3, (key, errs[key], predicted)
+
+
+@pytest.mark.parametrize("case", ["beta_one", "no_decay", "beta_one_no_decay"])
+def test_boundary_gates(oracle_mod, case):
+    """The method's boundary settings: beta = 1 (each write replaces the key's component of the
+    state) and g = 0 (no decay), alone and together, on ragged chunks with h0 and dS_final."""
+    inp = _small_inputs("dense_ragged")
+    if "beta_one" in case:
+        inp["beta"] = torch.ones_like(inp["beta"])
+    if "no_decay" in case:
+        inp["g"] = torch.zeros_like(inp["g"])
+    out = run_gpu(inp)
+    ref = run_oracle(oracle_mod, inp)
+    errs, bad = compare(inp, out, ref)
+    _report(case, errs)
+    assert not bad, bad
