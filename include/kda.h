@@ -79,7 +79,8 @@ typedef struct {
                             dbeta * beta (1 - beta). Other values: KDA_EINVAL.              */
 } kda_dims;
 
-/* Total number of chunks NT = sum_n ceil(len_n / C); -1 if dims are invalid. */
+/* Total number of chunks NT = sum_n ceil(len_n / C); -1 if dims are invalid. Valid dims have
+ * NT <= 2^30 and NT * HV <= 2^31 - 1 (the kernels launch one workgroup per chunk and head). */
 int64_t kda_num_chunks(const kda_dims* dims);
 
 /* Workspace bytes needed by kda_fwd_states / kda_chunk_bwd; 0 if dims are invalid. The

@@ -62,6 +62,7 @@ def _call_bwd(lib, d, ptr=1):
     (dict(dtype="f32"), -2, "unsupported"),
     (dict(T=-1), -1, "positive"),
     (dict(H=0), -1, "positive"),
+    (dict(B=1 << 20, T=1 << 11, H=8, HV=256), -1, "too many chunk-heads"),
 ])
 def test_validation_errors(lib, kw, status, msg):
     d, _ = _dims(**kw)
