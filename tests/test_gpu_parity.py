@@ -201,3 +201,49 @@ def test_boundary_gates(oracle_mod, case):
     errs, bad = compare(inp, out, ref)
     _report(case, errs)
     assert not bad, bad
+
+
+def _random_case(i):
+    """Seeded random geometry: precision, chunk size, heads and grouping, dense or packed
+    lengths (empty and one-token sequences included), initial state and final-state gradient,
+    beta or its logits."""
+    rng = np.random.default_rng(500 + i)
+    f32 = rng.random() < 0.25
+    dims = dict(K=16, V=16, C=16, dtype="f32") if f32 else dict(K=128, V=128, C=int(rng.choice([16, 64])),
+                                                                   dtype="bf16")
+    H = int(rng.integers(1, 4))
+    HV = H * int(rng.integers(1, 5))
+    has_h0, has_dsf = bool(rng.random() < 0.7), bool(rng.random() < 0.7)
+    if rng.random() < 0.5:
+        w = small_workload(f"rand{i}", B=int(rng.integers(1, 4)), T=int(rng.integers(1, 260)), H=H, HV=HV,
+                           has_h0=has_h0, has_dsf=has_dsf, **dims)
+        inp = kin.make_inputs(w, seed=600 + i)
+    else:
+        lens = [int(x) for x in rng.integers(0, 200, size=int(rng.integers(1, 6)))]
+        lens[int(rng.integers(0, len(lens)))] = int(rng.choice([0, 1, 64, 65]))
+        if sum(lens) == 0:
+            lens[0] = 7
+        cu = [0]
+        for ln in lens:
+            cu.append(cu[-1] + ln)
+        w = small_workload(f"rand{i}", varlen=len(lens), total=cu[-1], len_lo=0, len_hi=cu[-1], H=H, HV=HV,
+                           has_h0=has_h0, has_dsf=has_dsf, **dims)
+        inp = kin.make_inputs(w, seed=600 + i)
+        inp["cu_seqlens"] = cu
+    logits = bool(rng.random() < 0.3)
+    if logits:
+        inp["beta"] = torch.from_numpy(rng.normal(0.0, 1.5, size=tuple(inp["beta"].shape)).astype(np.float32))
+    return inp, logits
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_geometries(oracle_mod, i):
+    inp, logits = _random_case(i)
+    w = inp["workload"]
+    print(f"[rand {i}] {w.dtype} C={w.C} H={w.H} HV={w.HV} cu={inp['cu_seqlens']} B={inp['B']} T={inp['T']} "
+          f"h0={inp['h0'] is not None} dsf={inp['dS_final'] is not None} logits={logits}", flush=True)
+    out = run_gpu(inp, beta_logits=logits)
+    ref = run_oracle(oracle_mod, inp, beta_logits=logits)
+    errs, bad = compare(inp, out, ref)
+    _report(f"rand {i}", errs)
+    assert not bad, bad
