@@ -9,12 +9,15 @@ L2 nor the 256 MB Infinity Cache holds the inputs (cold-cache timing); the flush
 outside the timed interval, which HIP events bracket on the call's stream. Warm-cache
 (back-to-back) timing is reported alongside.
 
-Prints one JSON line. `value` is token-heads per second (tokens x value heads / time).
+Prints one JSON line. `value` is token-heads per second (tokens x value heads / median cold
+call time) on the B=2, T=2048, H=8, K=V=128, C=64 workload; the other three K=V=128
+workloads are measured the same way (fewer steps) under `per_workload`.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -28,27 +31,41 @@ sys.path.insert(0, HERE)
 PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E, bytes/s
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA, flop/s
 PEAK_F32_FLOPS = 157.3e12    # MI355X dense fp32 MFMA
+CPU_SHARE = 16               # host threads of one GPU's share of the box
+
+# Kernels of one kda_chunk_bwd call, in launch order (the chunk table only for packed sequences).
+BWD_KERNELS = ["bwd_prep", "bwd_scan", "bwd_grad"]
+# Sources whose text fixes the backward kernels and their workspace layout.
+BWD_SOURCES = ["kda_api.cpp", "kda_bwd.hip", "kda_scan.hip", "kda_device.h", "kda_launch.h"]
+TRAFFIC_RECORD = os.path.join(HERE, "profiles", "kda_chunk_bwd_w1_hbm_counters.md")
 
 
-def recorded_traffic(workload_name):
-    """HBM bytes per bwd_grad launch measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE,
-    scaled by a plain copy's readings) as recorded in profiles/bwd_grad_w1_counters.md, or None
-    when that record is for another workload or the kernel's sources have changed since."""
-    import hashlib
-    rec = os.path.join(HERE, "profiles", "bwd_grad_w1_counters.md")
-    if not os.path.exists(rec):
-        return None
+def sources_sha256():
     h = hashlib.sha256()
-    for f in ("kda_bwd.hip", "kda_device.h"):
+    for f in BWD_SOURCES:
         with open(os.path.join(HERE, "chunked_gated_delta_09_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    with open(rec) as fh:
+    return h.hexdigest()
+
+
+def recorded_traffic(workload_name, kernel="call", record=TRAFFIC_RECORD):
+    """HBM bytes per launch of `kernel` (or per call, the sum over the call's kernels)
+    measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE, scaled by a plain copy's
+    readings) as recorded in the counters profile, or None when the record is for another
+    workload or the backward's sources have changed since it was taken."""
+    if not os.path.exists(record):
+        return None
+    sha = sources_sha256()
+    per = {}
+    with open(record) as fh:
         for line in fh:
             if line.startswith("bench-traffic:"):
                 kv = dict(t.split("=", 1) for t in line.split()[1:])
-                if kv.get("workload") == workload_name and kv.get("sources-sha256") == h.hexdigest():
-                    return int(kv["bytes"])
-    return None
+                if kv.get("workload") == workload_name and kv.get("sources-sha256") == sha:
+                    per[kv["kernel"]] = int(kv["bytes"])
+    if kernel == "call":
+        return sum(per[k] for k in BWD_KERNELS) if all(k in per for k in BWD_KERNELS) else None
+    return per.get(kernel)
 
 
 def algorithmic_bytes(w, inp):
@@ -56,7 +73,7 @@ def algorithmic_bytes(w, inp):
     states and inverses, dS_final; writes of dq, dk, dv, dg, dbeta, dh0."""
     es = 4 if w.dtype == "f32" else 2
     T, N = inp["B"] * inp["T"], inp["N"]
-    nt = sum(math.ceil((b - a) / w.C) for a, b in zip(flat_cu(inp)[:-1], flat_cu(inp)[1:]))
+    nt = num_chunks(w, inp)
     reads = (2 * T * w.H * w.K * es + 2 * T * w.HV * w.V * es + T * w.HV * w.K * 4 + T * w.HV * 4
              + nt * w.HV * (w.K * w.V + w.C * w.C) * es)
     writes = 2 * T * w.H * w.K * es + T * w.HV * w.V * es + T * w.HV * w.K * 4 + T * w.HV * 4
@@ -72,6 +89,24 @@ def algorithmic_flops(w, inp):
     return (14 * w.K * w.V + 10 * w.C * w.K) * inp["B"] * inp["T"] * w.HV
 
 
+def fwd_algorithmic_bytes(w, inp):
+    """Bytes kda_fwd_states with the output o must move at least once: reads of q, k, v, g,
+    beta, h0; writes of the chunk states and inverses, o and the final state."""
+    es = 4 if w.dtype == "f32" else 2
+    T, N = inp["B"] * inp["T"], inp["N"]
+    nt = num_chunks(w, inp)
+    reads = 2 * T * w.H * w.K * es + T * w.HV * w.V * es + T * w.HV * w.K * 4 + T * w.HV * 4
+    if inp["h0"] is not None:
+        reads += N * w.HV * w.K * w.V * es
+    writes = nt * w.HV * (w.K * w.V + w.C * w.C) * es + T * w.HV * w.V * es + N * w.HV * w.K * w.V * 4
+    return reads + writes
+
+
+def num_chunks(w, inp):
+    cu = flat_cu(inp)
+    return sum(math.ceil((b - a) / w.C) for a, b in zip(cu[:-1], cu[1:]))
+
+
 def flat_cu(inp):
     from chunked_gated_delta_09_amd import inputs as kin
     return kin.flat_cu(inp)
@@ -79,22 +114,189 @@ def flat_cu(inp):
 
 def cpu_baseline(inp):
     """The fp64 oracle (forward + hand-derived backward) on the host cores, timed on the
-    whole workload: every (sequence, value head) task."""
+    whole workload: every (sequence, value head) task, on at most one GPU's share of the
+    host's threads."""
     import oracle
     from tests.kda_cases import run_oracle
     oracle.build(force=False)
-    # repeated until about a second of wall time (10-20 s of CPU work on the box's cores)
+    nthreads = max(1, min(CPU_SHARE, os.cpu_count() or 1))
+    # repeated until about a second of wall time (10-20 s of CPU work on the threads used)
     runs, t0 = 0, time.perf_counter()
     while True:
-        r = run_oracle(oracle, inp)
+        r = run_oracle(oracle, inp, nthreads=nthreads)
         runs += 1
         dt = time.perf_counter() - t0
         if dt > 1.0 and runs >= 2:
             break
     th = inp["B"] * inp["T"] * inp["workload"].HV
     return {"value": runs * th / dt, "unit": "token-heads/s", "cores": int(r["threads"]), "kind": "oracle",
+            "threads": int(r["threads"]), "host_nproc": os.cpu_count(),
             "sample": f"whole workload ({th} token-heads, {inp['N']} sequences x {inp['workload'].HV} heads), "
                       f"fp64 forward+backward, {runs} runs in {dt:.2f} s"}
+
+
+def _pct(xs, p):
+    s = sorted(xs)
+    return s[int(round(p * (len(s) - 1)))]
+
+
+class Hip:
+    """The HIP runtime torch has loaded, for events on the call's stream."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev.value
+        return arr
+
+    def record(self, ev, stream):
+        self.lib.hipEventRecord(ev, stream)
+
+    def elapsed(self, e0, e1):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), e0, e1) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, arr):
+        for e in arr:
+            self.lib.hipEventDestroy(e)
+
+
+def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True):
+    """Times kda_chunk_bwd on workload `wid`: cold and (optionally) warm call times, and the
+    per-kernel times from the library's event hook; optionally the forward with o."""
+    import torch
+    import chunked_gated_delta_09_amd as kda
+    from chunked_gated_delta_09_amd import inputs as kin
+    from chunked_gated_delta_09_amd import measure as kmeas
+
+    w = kin.WORKLOADS[wid]
+    inp = kin.make_inputs(w, wid=wid)
+    dev = torch.device("cuda:0")
+    d = {k: (inp[k].contiguous().to(dev) if inp[k] is not None else None)
+         for k in ("q", "k", "v", "g", "beta", "h0", "dS_final", "dO")}
+    fw = kda.fwd_states(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], cu_seqlens=inp["cu_seqlens"],
+                        C=w.C, scale=inp["scale"])
+    cu_dev = (torch.tensor(inp["cu_seqlens"], dtype=torch.int32, device=dev)
+              if inp["cu_seqlens"] is not None else None)
+    B, T = inp["B"], inp["T"]
+    dims, keep = kda.make_dims(B, T, w.H, w.HV, w.K, w.V, w.C, inp["scale"], w.dtype, inp["cu_seqlens"], cu_dev)
+    tdt = w.torch_dtype
+    dq = torch.empty(B, T, w.H, w.K, dtype=tdt, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty(B, T, w.HV, w.V, dtype=tdt, device=dev)
+    dg = torch.empty(B, T, w.HV, w.K, dtype=torch.float32, device=dev)
+    dbeta = torch.empty(B, T, w.HV, dtype=torch.float32, device=dev)
+    dh0 = torch.empty(inp["N"], w.HV, w.K, w.V, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.bwd_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    nk = 4 if inp["cu_seqlens"] is not None else 3  # kernels per call
+    names = (["chunk_table"] if nk == 4 else []) + BWD_KERNELS
+
+    def step():
+        kda.chunk_bwd_into(dims, d["q"], d["k"], d["v"], d["g"], d["beta"], fw["states"], fw["inv"], d["dO"],
+                           d["dS_final"], dq, dk, dv, dg, dbeta, dh0, ws, stream=stream)
+
+    def timed(nsteps, flush, per_kernel):
+        """nsteps calls; HIP events around each call on its stream, and (per_kernel) the
+        library's events around each of its kernels. The timed region is bracketed by
+        device synchronisation."""
+        call_ev = hip.events(2 * nsteps)
+        kern_ev = hip.events(2 * nk * nsteps) if per_kernel else None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(nsteps):
+            if flush:
+                flush_buf.fill_(i & 0xFF)
+            if per_kernel:
+                kmeas.set_kernel_events(
+                    ctypes.cast(ctypes.byref(kern_ev, 2 * nk * i * ctypes.sizeof(ctypes.c_void_p)),
+                                ctypes.POINTER(ctypes.c_void_p)), 2 * nk)
+            hip.record(call_ev[2 * i], stream)
+            step()
+            hip.record(call_ev[2 * i + 1], stream)
+        kmeas.set_kernel_events(None, 0)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        calls = [hip.elapsed(call_ev[2 * i], call_ev[2 * i + 1]) for i in range(nsteps)]
+        kern = {}
+        if per_kernel:
+            kern = {name: [hip.elapsed(kern_ev[2 * nk * i + 2 * j], kern_ev[2 * nk * i + 2 * j + 1])
+                           for i in range(nsteps)] for j, name in enumerate(names)}
+        hip.destroy(call_ev)
+        if kern_ev is not None:
+            hip.destroy(kern_ev)
+        return calls, kern, wall
+
+    for _ in range(warmup):
+        step()
+    res = {"workload": w, "inp": inp}
+    res["cold_calls"], _, res["cold_wall"] = timed(steps, flush=True, per_kernel=False)
+    _, res["cold_kern"], _ = timed(steps, flush=True, per_kernel=True)
+    if warm:
+        res["warm_calls"], _, _ = timed(steps, flush=False, per_kernel=False)
+        _, res["warm_kern"], _ = timed(steps, flush=False, per_kernel=True)
+    if forward:
+        # The training forward (kda_fwd_states with the output o), timed the same way
+        # (cold): reported beside the backward, not part of the step.
+        def fwd_step():
+            return kda.fwd_states(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"],
+                                  cu_seqlens=inp["cu_seqlens"], C=w.C, scale=inp["scale"], output_o=True)
+
+        for _ in range(2):
+            fwd_step()
+        fwd_ev = hip.events(2 * steps)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            flush_buf.fill_(i & 0xFF)
+            hip.record(fwd_ev[2 * i], stream)
+            fwd_step()
+            hip.record(fwd_ev[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        res["fwd_calls"] = [hip.elapsed(fwd_ev[2 * i], fwd_ev[2 * i + 1]) for i in range(steps)]
+        hip.destroy(fwd_ev)
+    del keep, fw, d, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def summarize(res):
+    """Median-based figures of one workload: call time, token-heads/s, the call's HBM
+    roofline fraction and per-kernel times."""
+    w, inp = res["workload"], res["inp"]
+    th = inp["B"] * inp["T"] * w.HV
+    ms = statistics.median(res["cold_calls"])
+    abytes = algorithmic_bytes(w, inp)
+    aflops = algorithmic_flops(w, inp)
+    peak_flops = PEAK_F32_FLOPS if w.dtype == "f32" else PEAK_BF16_FLOPS
+    t_roof = max(abytes / PEAK_HBM_BYTES, aflops / peak_flops)
+    out = {"workload": w.name, "token_heads": th, "ms_cold_median": ms,
+           "ms_cold_p10_p90": [_pct(res["cold_calls"], 0.1), _pct(res["cold_calls"], 0.9)],
+           "token_heads_per_s": th / (ms * 1e-3), "algorithmic_bytes": abytes, "algorithmic_flops": aflops,
+           "t_roofline_ms": t_roof * 1e3, "call_frac": t_roof / (ms * 1e-3),
+           "kernels_ms_cold": {k: statistics.median(v) for k, v in res["cold_kern"].items()}}
+    if "warm_calls" in res:
+        out["ms_warm_median"] = statistics.median(res["warm_calls"])
+        out["kernels_ms_warm"] = {k: statistics.median(v) for k, v in res["warm_kern"].items()}
+    if "fwd_calls" in res:
+        fms = statistics.median(res["fwd_calls"])
+        fb = fwd_algorithmic_bytes(w, inp)
+        out["forward"] = {"entry": "kda_fwd_states with o (chunk prep, forward state scan, output)",
+                          "ms_cold_median": fms, "token_heads_per_s": th / (fms * 1e-3),
+                          "algorithmic_bytes": fb, "achieved_GBps": fb / (fms * 1e-3) / 1e9,
+                          "hbm_frac": fb / (fms * 1e-3) / PEAK_HBM_BYTES}
+    return out
 
 
 def main():
@@ -103,6 +305,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1, help="workload id (1 = B=2,T=2048,H=8,K=V=128,C=64)")
+    ap.add_argument("--others", default="2,3,4",
+                    help="further workload ids measured under per_workload ('' for none)")
+    ap.add_argument("--other-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (for scaling the "
@@ -123,129 +328,30 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": args.copy_calibration << 20, "copies": 3}), flush=True)
         return
-    import chunked_gated_delta_09_amd as kda
-    from chunked_gated_delta_09_amd import inputs as kin
 
-    w = kin.WORKLOADS[args.workload]
-    inp = kin.make_inputs(w, wid=args.workload)
-    dev = torch.device("cuda:0")
-    d = {k: (inp[k].contiguous().to(dev) if inp[k] is not None else None)
-         for k in ("q", "k", "v", "g", "beta", "h0", "dS_final", "dO")}
-    fw = kda.fwd_states(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], cu_seqlens=inp["cu_seqlens"],
-                        C=w.C, scale=inp["scale"])
-    cu_dev = (torch.tensor(inp["cu_seqlens"], dtype=torch.int32, device=dev)
-              if inp["cu_seqlens"] is not None else None)
-    B, T = inp["B"], inp["T"]
-    dims, keep = kda.make_dims(B, T, w.H, w.HV, w.K, w.V, w.C, inp["scale"], w.dtype, inp["cu_seqlens"], cu_dev)
-    tdt = w.torch_dtype
-    dq = torch.empty(B, T, w.H, w.K, dtype=tdt, device=dev)
-    dk = torch.empty_like(dq)
-    dv = torch.empty(B, T, w.HV, w.V, dtype=tdt, device=dev)
-    dg = torch.empty(B, T, w.HV, w.K, dtype=torch.float32, device=dev)
-    dbeta = torch.empty(B, T, w.HV, dtype=torch.float32, device=dev)
-    dh0 = torch.empty(inp["N"], w.HV, w.K, w.V, dtype=torch.float32, device=dev)
-    ws = torch.empty(kda.bwd_workspace_bytes(dims), dtype=torch.uint8, device=dev)
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    hip = Hip()
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=torch.device("cuda:0"))
+    main_res = measure(args.workload, args.steps, args.warmup, hip, flush_buf)
+    s = summarize(main_res)
+    w, inp = main_res["workload"], main_res["inp"]
+    others = [int(x) for x in args.others.split(",") if x.strip()]
+    per_workload = {}
+    for wid in others:
+        if wid == args.workload:
+            continue
+        r = measure(wid, args.other_steps, 2, hip, flush_buf, warm=False, forward=True)
+        per_workload[str(wid)] = summarize(r)
+        del r
 
-    lib = kda.load()
-    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded
-    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    stream = torch.cuda.current_stream().cuda_stream
-    nk = 4 if inp["cu_seqlens"] is not None else 3  # kernels per call
-    kernel_names = (["chunk_table"] if nk == 4 else []) + ["bwd_prep", "bwd_scan", "bwd_grad"]
-
-    def new_events(n):
-        arr = (ctypes.c_void_p * n)()
-        for i in range(n):
-            ev = ctypes.c_void_p()
-            if hip.hipEventCreate(ctypes.byref(ev)) != 0:
-                raise RuntimeError("hipEventCreate failed")
-            arr[i] = ev.value
-        return arr
-
-    def elapsed(e0, e1):
-        ms = ctypes.c_float()
-        if hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return ms.value
-
-    def step():
-        kda.chunk_bwd_into(dims, d["q"], d["k"], d["v"], d["g"], d["beta"], fw["states"], fw["inv"], d["dO"],
-                           d["dS_final"], dq, dk, dv, dg, dbeta, dh0, ws, stream=stream)
-
-    def timed(nsteps, flush, per_kernel):
-        """nsteps calls; HIP events around each call on its stream, and (per_kernel) the
-        library's events around each of its kernels. The timed region is bracketed by
-        device synchronisation."""
-        call_ev = new_events(2 * nsteps)
-        kern_ev = new_events(2 * nk * nsteps) if per_kernel else None
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(nsteps):
-            if flush:
-                flush_buf.fill_(i & 0xFF)
-            if per_kernel:
-                lib.kda_set_kernel_events(
-                    ctypes.cast(ctypes.byref(kern_ev, 2 * nk * i * ctypes.sizeof(ctypes.c_void_p)),
-                                ctypes.POINTER(ctypes.c_void_p)), 2 * nk)
-            hip.hipEventRecord(call_ev[2 * i], stream)
-            step()
-            hip.hipEventRecord(call_ev[2 * i + 1], stream)
-        lib.kda_set_kernel_events(None, 0)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        calls = [elapsed(call_ev[2 * i], call_ev[2 * i + 1]) for i in range(nsteps)]
-        kern = {}
-        if per_kernel:
-            kern = {name: [elapsed(kern_ev[2 * nk * i + 2 * j], kern_ev[2 * nk * i + 2 * j + 1])
-                           for i in range(nsteps)] for j, name in enumerate(kernel_names)}
-        for arr in (call_ev, kern_ev or []):
-            for e in arr:
-                hip.hipEventDestroy(e)
-        return calls, kern, wall
-
-    for _ in range(args.warmup):
-        step()
-    cold_calls, _, cold_wall = timed(args.steps, flush=True, per_kernel=False)
-    warm_calls, _, _ = timed(args.steps, flush=False, per_kernel=False)
-    _, cold_kern, _ = timed(args.steps, flush=True, per_kernel=True)
-    _, warm_kern, _ = timed(args.steps, flush=False, per_kernel=True)
-
-    # The training forward (kda_fwd_states with the output o), timed the same way (cold):
-    # reported beside the backward, not part of the step.
-    def fwd_step():
-        return kda.fwd_states(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], cu_seqlens=inp["cu_seqlens"],
-                              C=w.C, scale=inp["scale"], output_o=True)
-
-    for _ in range(2):
-        fwd_step()
-    fwd_ev = new_events(2 * args.steps)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        flush_buf.fill_(i & 0xFF)
-        hip.hipEventRecord(fwd_ev[2 * i], stream)
-        fwd_step()
-        hip.hipEventRecord(fwd_ev[2 * i + 1], stream)
-    torch.cuda.synchronize()
-    fwd_ms = statistics.mean(elapsed(fwd_ev[2 * i], fwd_ev[2 * i + 1]) for i in range(args.steps))
-    for e in fwd_ev:
-        hip.hipEventDestroy(e)
-
-    th = B * T * w.HV
-    ms = statistics.mean(cold_calls)
-    value = th / (ms * 1e-3)
-    abytes = algorithmic_bytes(w, inp)
-    aflops = algorithmic_flops(w, inp)
-    grad_ms = statistics.mean(cold_kern["bwd_grad"])
-    achieved = abytes / (grad_ms * 1e-3) / 1e9
-    peak_flops = PEAK_F32_FLOPS if w.dtype == "f32" else PEAK_BF16_FLOPS
-    t_roof = max(abytes / PEAK_HBM_BYTES, aflops / peak_flops)
+    ms = s["ms_cold_median"]
+    abytes = s["algorithmic_bytes"]
+    achieved = abytes / (ms * 1e-3) / 1e9
+    grad_ms = s["kernels_ms_cold"]["bwd_grad"]
+    grad_achieved = abytes / (grad_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(w.name, "call")
     out = {
         "metric": "KDA chunk-bwd token-heads/s at K=V=128, C=64 (HBM roofline fraction)",
-        "value": value,
+        "value": s["token_heads_per_s"],
         "unit": "token-heads/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -257,28 +363,36 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v,dO N(0,1), g=logsigmoid(N(3,1)), "
                 "beta=sigmoid(N(0,1)), h0,dS_final N(0,0.1))",
-        "config": {"workload": w.name, "B": B, "T": T, "H": w.H, "HV": w.HV, "K": w.K, "V": w.V, "C": w.C,
-                   "token_heads": th, "cache": "cold (1 GiB flush before each step, outside the timed interval)"},
-        "roofline": {"bound": "hbm", "kernel": "bwd_grad", "achieved": achieved, "peak": PEAK_HBM_BYTES / 1e9,
-                     "unit": "GB/s", "frac": achieved / (PEAK_HBM_BYTES / 1e9), "traffic": recorded_traffic(w.name),
-                     "algorithmic_bytes_per_launch": abytes,
-                     "launch_ms": grad_ms},
-        "call_roofline": {"t_roofline_ms": t_roof * 1e3, "frac": t_roof / (ms * 1e-3),
-                          "algorithmic_bytes": abytes, "algorithmic_flops": aflops},
-        "kernels_ms_cold": {k: statistics.mean(v) for k, v in cold_kern.items()},
-        "kernels_ms_warm": {k: statistics.mean(v) for k, v in warm_kern.items()},
-        "ms_per_step_p10_p50_p90_cold": [sorted(cold_calls)[int(0.1 * (len(cold_calls) - 1))],
-                                         statistics.median(cold_calls),
-                                         sorted(cold_calls)[int(0.9 * (len(cold_calls) - 1))]],
-        "ms_per_step_warm": statistics.mean(warm_calls),
-        "forward": {"entry": "kda_fwd_states with o (chunk prep, forward state scan, output)",
-                    "ms_cold": fwd_ms, "token_heads_per_s": th / (fwd_ms * 1e-3)},
-        "wall_s_timed_cold_incl_flush": cold_wall,
+        "config": {"workload": w.name, "B": inp["B"], "T": inp["T"], "H": w.H, "HV": w.HV, "K": w.K, "V": w.V,
+                   "C": w.C, "token_heads": s["token_heads"],
+                   "cache": "cold (1 GiB flush before each step, outside the timed interval)",
+                   "timing": "median of the timed steps"},
+        # The whole kda_chunk_bwd call is the unit: its algorithmic bytes over its median cold
+        # time, against the HBM peak; traffic is the counters' HBM bytes of one call (the
+        # three kernels' FETCH_SIZE and WRITE_SIZE, calibrated), null if the sources changed.
+        "roofline": {"bound": "hbm", "unit": "GB/s", "achieved": achieved, "peak": PEAK_HBM_BYTES / 1e9,
+                     "frac": achieved / (PEAK_HBM_BYTES / 1e9), "traffic": traffic,
+                     "scope": "kda_chunk_bwd call (prep + reverse scan + gradients)",
+                     "algorithmic_bytes_per_call": abytes, "call_ms": ms,
+                     "traffic_over_algorithmic": (traffic / abytes) if traffic else None,
+                     "dominant_kernel": {"kernel": "bwd_grad", "launch_ms": grad_ms,
+                                         "achieved": grad_achieved,
+                                         "frac": grad_achieved / (PEAK_HBM_BYTES / 1e9),
+                                         "traffic": recorded_traffic(w.name, "bwd_grad"),
+                                         "note": "every algorithmic byte of the call credited to this one "
+                                                 "kernel's time"},
+                     "flops_frac_bf16": s["algorithmic_flops"] / (ms * 1e-3) / PEAK_BF16_FLOPS},
+        "ms_per_step_p10_p50_p90_cold": [s["ms_cold_p10_p90"][0], ms, s["ms_cold_p10_p90"][1]],
+        "ms_per_step_warm_median": s["ms_warm_median"],
+        "kernels_ms_cold": s["kernels_ms_cold"],
+        "kernels_ms_warm": s["kernels_ms_warm"],
+        "forward": s["forward"],
+        "per_workload": per_workload,
+        "wall_s_timed_cold_incl_flush": main_res["cold_wall"],
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)
-    del keep
 
 
 if __name__ == "__main__":

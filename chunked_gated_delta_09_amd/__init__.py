@@ -60,8 +60,6 @@ def load():
         lib.kda_fwd_states.argtypes = [dp] + [vp] * 10 + [vp, sz, vp]
         lib.kda_chunk_bwd.restype = ctypes.c_int
         lib.kda_chunk_bwd.argtypes = [dp] + [vp] * 15 + [vp, sz, vp]
-        lib.kda_set_kernel_events.restype = None
-        lib.kda_set_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
         _lib = lib
     return _lib
 

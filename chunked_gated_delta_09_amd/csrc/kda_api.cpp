@@ -9,6 +9,7 @@
 #include <string>
 
 #include "kda.h"
+#include "kda_measure.h"
 #include "kda_launch.h"
 
 #define KDA_EXPORT extern "C" __attribute__((visibility("default")))
@@ -19,7 +20,7 @@ thread_local std::string g_err;
 thread_local void* const* g_events = nullptr;
 thread_local int g_nevents = 0;
 
-// Records the measurement events around the i-th launch of a call (see kda.h).
+// Records the measurement events around the i-th launch of a call (kda_measure.h).
 struct LaunchCounter {
   hipStream_t st;
   int i = 0;
@@ -182,6 +183,22 @@ kda_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 }  // namespace
 
+namespace kda {
+
+// Validation and workspace size of a kda_chunk_bwd call, for entry points that supply the
+// workspace themselves (the message of a failed check is left for kda_last_error).
+kda_status bwd_plan(const kda_dims* dims, size_t* ws_bytes) {
+  Plan p;
+  const kda_status st = validate(dims, p, true);
+  if (st != KDA_OK) return st;
+  *ws_bytes = bwd_layout(dims, p).total;
+  return KDA_OK;
+}
+
+kda_status set_error(kda_status st, const char* msg) { return fail(st, "%s", msg); }
+
+}  // namespace kda
+
 KDA_EXPORT int64_t kda_num_chunks(const kda_dims* dims) {
   Plan p;
   if (validate(dims, p, false) != KDA_OK) return -1;
@@ -281,5 +298,24 @@ KDA_EXPORT kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const v
   KDA_HIP(kda::launch_bwd_prep(p.dtype, p.C, s, q, k, g, beta, inv, dO, bw, hs));
   KDA_HIP(kda::launch_scan_bwd(p.dtype, p.C, s, bw, dS_final, dh0, hs));
   KDA_HIP(kda::launch_bwd_grad(p.dtype, p.C, s, q, k, v, g, beta, states, inv, dO, bw, dq, dk, dv, dg, dbeta, hs));
+  return KDA_OK;
+}
+
+KDA_EXPORT kda_status kda_bwd_state_grads(const kda_dims* dims, const void* workspace, size_t ws_bytes,
+                                          float* dstates, void* stream) {
+  Plan p;
+  kda_status st = validate(dims, p, true);
+  if (st != KDA_OK) return st;
+  if (p.NT > 0) KDA_REQUIRE(dstates, "dstates");
+  const BwdLayout L = bwd_layout(dims, p);
+  st = check_ws(const_cast<void*>(workspace), ws_bytes, L.total);
+  if (st != KDA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  LaunchCounter lc(hs);
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  const kda::Shape s = make_shape(dims, p, ws, L.choff);
+  kda::BwdWs bw{};
+  bw.dS = ws + L.dS;
+  KDA_HIP(kda::launch_dstates_out(p.dtype, p.C, s, bw, dstates, hs));
   return KDA_OK;
 }

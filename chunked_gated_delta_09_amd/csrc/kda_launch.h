@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda.h"
+
 namespace kda {
 
 // Problem geometry shared by every kernel.
@@ -53,5 +55,12 @@ hipError_t launch_scan_bwd(int dtype, int C, const Shape& s, const BwdWs& ws, co
 hipError_t launch_bwd_grad(int dtype, int C, const Shape& s, const void* q, const void* k, const void* v,
                            const float* g, const float* beta, const void* states, const void* inv, const void* dO,
                            const BwdWs& ws, void* dq, void* dk, void* dv, float* dg, float* dbeta, hipStream_t st);
+
+hipError_t launch_dstates_out(int dtype, int C, const Shape& s, const BwdWs& ws, float* out, hipStream_t st);
+
+// C-ABI helpers (kda_api.cpp): validation + workspace size of a kda_chunk_bwd call, and the
+// thread-local error message behind kda_last_error.
+kda_status bwd_plan(const kda_dims* dims, size_t* ws_bytes);
+kda_status set_error(kda_status st, const char* msg);
 
 }  // namespace kda

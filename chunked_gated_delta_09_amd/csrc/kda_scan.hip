@@ -5,7 +5,7 @@
 //   Y    = Z + P1 X                 (C x V, contraction over K)
 //   X'   = diag(e^gam) X + W + P2 Y (K x V, contraction over C)
 // Forward (FLA chunk_gated_delta_rule_fwd_h; FlashKDA page, the state update
-// S_new = S*exp(gT) + kr^T@U): X = S, P1 = -w, Z = u, P2 = kr^T, W = 0, so Y = U and
+// S_out = diag(e^gam) S_in + kr^T U): X = S, P1 = -w, Z = u, P2 = kr^T, W = 0, so Y = U and
 // X' = S_out. Backward (FLA chunk_gated_delta_rule_bwd_dhu; FlashKDA page steps 2-3):
 // X = dS (gradient w.r.t. S_out), P1 = kr, Z = 0 so Y = kr dS, P2 = -w^T and
 // W = (qd - Mqk w)^T dO, giving X' = dS_in = diag(e^gam) dS + qd^T dO - w^T (Mqk^T dO + kr dS).
@@ -543,6 +543,41 @@ static hipError_t scan_t(const Shape& s, const void* P1, const void* P2, const v
                        static_cast<const T*>(Wi), eg, static_cast<const T*>(X0), static_cast<T*>(Xout),
                        static_cast<T*>(Yout), Xfin);
   }
+  return hipGetLastError();
+}
+
+// The per-chunk state gradients the reverse scan leaves in the backward workspace, written
+// out as plain [NT, HV, K, V] fp32 (an inspection aid for stage checks; the backward itself
+// never calls it). bf16 path: each chunk-head's gradient is in the scan's seed order, slice
+// ScanCols::slice(v) holding column v at lane column ScanCols::lane_col(v).
+template <class T, int K, int V, int C>
+__global__ __launch_bounds__(256) void dstates_out_kernel(const T* __restrict__ dS, float* __restrict__ out) {
+  const long base = (long)blockIdx.x * K * V;
+  for (int e = threadIdx.x; e < K * V; e += 256) {
+    const int k = e / V, v = e % V;
+    float x;
+    if constexpr (sizeof(T) == 2) {
+      const int lane = ScanCols::lane_col(v) + 16 * ((k & 15) >> 2);
+      x = (float)dS[base + ScanFrag<K, V, C>::seed(ScanCols::slice(v), k >> 4, K / 16, lane) + (k & 3)];
+    } else {
+      x = dS[base + e];
+    }
+    out[base + e] = x;
+  }
+}
+
+hipError_t launch_dstates_out(int dtype, int C, const Shape& s, const BwdWs& ws, float* out, hipStream_t st) {
+  const long nch = (long)s.NT * s.HV;
+  if (nch == 0) return hipSuccess;
+  if (dtype == 0)
+    hipLaunchKernelGGL((dstates_out_kernel<float, 16, 16, 16>), dim3(nch), dim3(256), 0, st,
+                       static_cast<const float*>(ws.dS), out);
+  else if (C == 64)
+    hipLaunchKernelGGL((dstates_out_kernel<bf16, 128, 128, 64>), dim3(nch), dim3(256), 0, st,
+                       static_cast<const bf16*>(ws.dS), out);
+  else
+    hipLaunchKernelGGL((dstates_out_kernel<bf16, 128, 128, 16>), dim3(nch), dim3(256), 0, st,
+                       static_cast<const bf16*>(ws.dS), out);
   return hipGetLastError();
 }
 

@@ -142,18 +142,6 @@ kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const void* k, con
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* kda_last_error(void);
 
-/*
- * Measurement hook (not needed for normal use). While `events` is non-NULL, every
- * kda_fwd_states / kda_chunk_bwd call made on this thread records, on its stream,
- * events[2*i] right before and events[2*i+1] right after its i-th kernel launch, for
- * i < count / 2, so a caller can time each kernel with hipEventElapsedTime. The handles
- * are hipEvent_t values created by the caller; the array must stay valid while it is set.
- * Launch order of kda_chunk_bwd: [chunk table, packed sequences only], backward
- * preparation, reverse state-gradient scan, chunk gradients. Of kda_fwd_states:
- * [chunk table], forward preparation, forward state scan, [output o].
- * Pass NULL (or count 0) to stop recording.
- */
-void kda_set_kernel_events(void* const* events, int count);
 
 #ifdef __cplusplus
 }

@@ -1,11 +1,11 @@
 """fp64 chunkwise form of KDA forward and backward (TEST INFRASTRUCTURE ONLY).
 
 Follows the chunk algebra of the FlashKDA backward page (step 1: recompute U; step 2:
-the gradient products; step 3: the adjoint of the triangular solve; the forward it
-differentiates, out = qd@S_in + Mqk@U, S_new = S*exp(gT) + kr^T@U, L = tril(kd@ki^T,-1)*beta)
-and of the FLA chunk_kda_bwd page (kernel chunk_kda_bwd_kernel_wy_dqkg_fused: the inter
-terms and the dg formula; driver chunk_kda_bwd: GVA reduction and the reverse chunk-local
-cumsum of dg). Notation, per sequence n, v-head h and chunk c with L valid rows:
+the gradient products; step 3: the adjoint of the triangular solve; the chunk forward it
+differentiates, written below as O, S_out and Lm in this module's notation) and of the FLA
+chunk_kda_bwd page (kernel chunk_kda_bwd_kernel_wy_dqkg_fused: the inter terms and the dg
+formula; driver chunk_kda_bwd: GVA reduction and the reverse chunk-local cumsum of dg).
+Notation, per sequence n, v-head h and chunk c with L valid rows:
 
   G = chunk-local inclusive cumsum of g; gam = G[L-1]
   qd = scale*q*e^G; kd = k*e^G; ki = k*e^-G; kr = k*e^(gam-G)

@@ -4,8 +4,9 @@
  * CPU-baseline leg of the benchmark may call it; the product path never does.
  *
  * Definition (KDA recurrence, as stated for the gated delta rule with per-channel decay;
- * FlashKDA backward page, the forward it differentiates: out = qd@S_in + Mqk@U and
- * S_new = S*exp(gT) + kr^T@U; FLA chunk_kda_bwd page, driver chunk_kda_bwd):
+ * the FlashKDA backward page differentiates its chunk form, in which a chunk's output is
+ * O = qd S_in + Mqk U and its outgoing state is diag(e^gam) S_in + kr^T U; FLA
+ * chunk_kda_bwd page, driver chunk_kda_bwd):
  *
  *   S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,   S is K x V
  *   o_t = scale * S_t^T q_t                     (S_t after token t's own write)

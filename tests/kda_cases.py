@@ -60,7 +60,7 @@ def head_slices(inp, qk_heads=None):
     return list(qk_heads), v_heads
 
 
-def run_oracle(oracle_mod, inp, qk_heads=None, beta_logits=False):
+def run_oracle(oracle_mod, inp, qk_heads=None, beta_logits=False, nthreads=0):
     """fp64 oracle on the given q/k heads (and their value heads), all sequences."""
     w = inp["workload"]
     qh, vh = head_slices(inp, qk_heads)
@@ -73,7 +73,8 @@ def run_oracle(oracle_mod, inp, qk_heads=None, beta_logits=False):
     dsf = None if inp["dS_final"] is None else _np(inp["dS_final"])[:, vh]
     cont = lambda a: None if a is None else np.ascontiguousarray(a)
     return oracle_mod.run(cont(q), cont(k), cont(v), cont(g), cont(beta), kin.flat_cu(inp), inp["scale"],
-                          h0=cont(h0), dO=cont(dO), dS_final=cont(dsf), beta_logits=beta_logits)
+                          h0=cont(h0), dO=cont(dO), dS_final=cont(dsf), beta_logits=beta_logits,
+                          nthreads=nthreads)
 
 
 def gpu_on_heads(inp, out, qk_heads=None):
@@ -93,19 +94,58 @@ def gpu_on_heads(inp, out, qk_heads=None):
     return res
 
 
-def compare(inp, out, ref, qk_heads=None, keys=None, tol=None):
-    """Relative L2 error of each compared tensor; returns dict key -> error."""
+# Floor of a chunk's reference norm in the per-chunk error, as a fraction of the chunk's
+# share of the whole tensor's norm (sqrt(rows of the chunk / rows of the tensor) of it):
+# a chunk whose gradient is genuinely tiny is then judged against the tensor's scale
+# instead of its own, while a wrong row (about 1/8 of a 64-row chunk's norm) or a wrong
+# partial tail still counts against the chunk it sits in.
+CHUNK_FLOOR = 0.25
+TOKEN_KEYS = ("dq", "dk", "dv", "dg", "dbeta", "o")
+
+
+def chunk_errors(x, ref, cu, C):
+    """Per-(chunk, head) relative L2 errors of a token-major tensor [T, heads, ...] (fp64),
+    with the chunk reference norm floored as described at CHUNK_FLOOR. Returns an array
+    [chunks, heads]."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    T = ref.shape[0]
+    heads = ref.shape[1]
+    x = x.reshape(T, heads, -1)
+    ref = ref.reshape(T, heads, -1)
+    full = np.sqrt(np.sum(ref ** 2, axis=(0, 2)))  # per head
+    out = []
+    for a, b in zip(cu[:-1], cu[1:]):
+        for s in range(a, b, C):
+            e = min(s + C, b)
+            num = np.sqrt(np.sum((x[s:e] - ref[s:e]) ** 2, axis=(0, 2)))
+            den = np.sqrt(np.sum(ref[s:e] ** 2, axis=(0, 2)))
+            floor = CHUNK_FLOOR * full * np.sqrt((e - s) / max(T, 1))
+            den = np.maximum(den, floor)
+            out.append(np.where(den > 0, num / np.where(den > 0, den, 1.0), num))
+    return np.array(out).reshape(-1, heads)
+
+
+def compare(inp, out, ref, qk_heads=None, keys=None, tol=None, per_chunk=True):
+    """Relative L2 error of each compared tensor, and (per_chunk) the largest per-(chunk,
+    head) relative L2 error of each token-major tensor under the key '<name>@chunk'.
+    Returns (errors, failures): every error is held to the same tolerance."""
     w = inp["workload"]
     tol = TOL[w.dtype] if tol is None else tol
     got = gpu_on_heads(inp, out, qk_heads)
     pairs = {"dq": "dq", "dk": "dk", "dv": "dv", "dg": "dg", "dbeta": "dbeta", "dh0": "dh0", "o": "o",
              "final_state": "S_T"}
     errs = {}
+    cu = kin.flat_cu(inp)
     for key, rkey in pairs.items():
         if keys is not None and key not in keys:
             continue
         if key not in got or got[key] is None:
             continue
         errs[key] = rel_l2(got[key], ref[rkey])
+        if per_chunk and key in TOKEN_KEYS and np.asarray(ref[rkey]).shape[0] > 0:
+            ce = chunk_errors(got[key], ref[rkey], cu, w.C)
+            if ce.size:
+                errs[key + "@chunk"] = float(ce.max())
     bad = {k: v for k, v in errs.items() if not v <= tol}
     return errs, bad

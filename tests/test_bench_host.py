@@ -60,10 +60,35 @@ def test_algorithmic_flops_count():
     assert bench.algorithmic_flops(w, inp) == per_chunk * chunks
 
 
-def test_recorded_traffic_follows_the_sources():
+def test_recorded_traffic_follows_the_sources(tmp_path):
     bench = _bench()
     w = kin.WORKLOADS[1]
     t = bench.recorded_traffic(w.name)
     # either the record matches the current sources (a positive byte count) or it is withheld
     assert t is None or t > bench.algorithmic_bytes(w, kin.make_inputs(w, wid=1))
     assert bench.recorded_traffic("no_such_workload") is None
+    # a record is used only with a line for every kernel of the call and the current sources
+    sha = bench.sources_sha256()
+    rec = tmp_path / "rec.md"
+    lines = [f"bench-traffic: workload={w.name} kernel={k} bytes={b} sources-sha256={sha}"
+             for k, b in zip(bench.BWD_KERNELS, (10, 20, 30))]
+    rec.write_text("\n".join(lines[:2]) + "\n")
+    assert bench.recorded_traffic(w.name, "call", record=str(rec)) is None
+    assert bench.recorded_traffic(w.name, "bwd_scan", record=str(rec)) == 20
+    rec.write_text("\n".join(lines) + "\n")
+    assert bench.recorded_traffic(w.name, "call", record=str(rec)) == 60
+    rec.write_text("\n".join(x.replace(sha, "0" * 64) for x in lines) + "\n")
+    assert bench.recorded_traffic(w.name, "call", record=str(rec)) is None
+
+
+def test_forward_algorithmic_bytes():
+    """kda_fwd_states with o: reads q, k, v (bf16), g, beta (fp32), h0; writes the chunk states
+    (K x V per chunk), inverses (C x C), o and the fp32 final state."""
+    bench = _bench()
+    w = kin.WORKLOADS[1]
+    inp = kin.make_inputs(w, wid=1)
+    th = inp["B"] * inp["T"] * w.HV
+    per_th = 2 * w.K * 2 + w.V * 2 + 4 * w.K + 4 + (w.K * w.V + w.C * w.C) * 2 / w.C + w.V * 2
+    per_seq = w.HV * w.K * w.V * (2 + 4)
+    assert per_th == 2180
+    assert bench.fwd_algorithmic_bytes(w, inp) == round(th * per_th + inp["N"] * per_seq)

@@ -1,8 +1,9 @@
 """GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
 
-Tolerances (relative L2 per tensor): 1e-4 for fp32 workloads, 2e-2 for bf16 ones.
-Small cases span several chunks and ragged tails; the five full workloads run at full
-size on the GPU with the oracle evaluated on sampled heads (every sequence of those heads).
+Tolerances (relative L2): 1e-4 for fp32 workloads, 2e-2 for bf16 ones, held by every
+tensor as a whole and by each of its (chunk, head) pieces (tests/kda_cases.compare). Small
+cases span several chunks and ragged tails; the five full workloads run at full size on the
+GPU with the oracle evaluated on sampled heads (every sequence of those heads).
 """
 import numpy as np
 import pytest
@@ -80,6 +81,45 @@ def test_stage_parity_states_and_inverse(oracle_mod):
     assert e_states < 1e-2 and e_inv < 1e-2
 
 
+@pytest.mark.parametrize("name", ["varlen_edges", "gva3_varlen", "c16"])
+def test_stage_parity_state_gradients(name):
+    """Per-chunk state gradients of the reverse scan (the dS_out each chunk's products consume;
+    FlashKDA backward page, step 2) against the fp64 chunked reference's, on packed ragged
+    sequences (an empty and a one-token sequence among them), grouped heads and C = 16."""
+    import chunked_gated_delta_09_amd as kda
+    from chunked_gated_delta_09_amd.measure import bwd_state_grads
+    from tests.kda_cases import chunk_errors, to_dev
+    inp = _small_inputs(name)
+    w = inp["workload"]
+    q, k, v, g, beta, h0, dsf, dO = (to_dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "h0", "dS_final", "dO"))
+    f = kda.fwd_states(q, k, v, g, beta, h0=h0, cu_seqlens=inp["cu_seqlens"], C=w.C, scale=inp["scale"])
+    cu = inp["cu_seqlens"]
+    cu_dev = torch.tensor(cu, dtype=torch.int32, device="cuda") if cu is not None else None
+    dims, keep = kda.make_dims(inp["B"], inp["T"], w.H, w.HV, w.K, w.V, w.C, inp["scale"], w.dtype, cu, cu_dev)
+    outs = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+                dh0=torch.empty(inp["N"], w.HV, w.K, w.V, dtype=torch.float32, device="cuda"))
+    ws = torch.empty(kda.bwd_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    kda.chunk_bwd_into(dims, q, k, v, g, beta, f["states"], f["inv"], dO, dsf, outs["dq"], outs["dk"], outs["dv"],
+                       outs["dg"], outs["dbeta"], outs["dh0"], ws)
+    got = bwd_state_grads(dims, ws).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    B, T = inp["B"], inp["T"]
+    fl = lambda t: t.float().numpy().astype(np.float64).reshape(B * T, *t.shape[2:])
+    ref = chunked_fwd_bwd(fl(inp["q"]), fl(inp["k"]), fl(inp["v"]), fl(inp["g"]),
+                          fl(inp["beta"]).reshape(B * T, -1), kin.flat_cu(inp), inp["scale"], w.C,
+                          h0=None if inp["h0"] is None else inp["h0"].double().numpy(), dO=fl(inp["dO"]),
+                          dS_final=None if inp["dS_final"] is None else inp["dS_final"].double().numpy())
+    e = rel_l2(got, ref["dstates"])
+    # each chunk-head's K x V gradient judged on its own (a chunk is one row of this tensor)
+    per = chunk_errors(got.reshape(got.shape[0], w.HV, -1), ref["dstates"].reshape(got.shape[0], w.HV, -1),
+                       [0, got.shape[0]], 1)
+    print(f"[stage dS {name}] all={e:.2e} worst chunk-head={per.max():.2e}", flush=True)
+    assert got.shape == ref["dstates"].shape
+    assert e < 1e-2 and per.max() < 1e-2
+    del keep
+
+
 def test_chunk_size_invariance_bf16(oracle_mod):
     """C = 16 and C = 64 are two tilings of the same map."""
     w = small_workload("cinv", B=1, T=160, H=1, HV=2, has_h0=True, has_dsf=True)
@@ -114,8 +154,10 @@ def test_empty_input():
     del kda
 
 
-# Full-size workloads: GPU on everything, oracle on sampled q/k heads.
-FULL_SAMPLES = {1: [0, 5], 2: [3], 3: [7], 4: [2]}
+# Full-size workloads: GPU on everything, oracle on sampled q/k heads (the last head of
+# every workload among them), every sequence of those heads, judged per tensor and per
+# (chunk, head).
+FULL_SAMPLES = {1: [0, 5, 7], 2: [3, 15], 3: [7, 15], 4: [2, 7]}
 
 
 @pytest.mark.parametrize("wid", [1, 2, 3, 4])
