@@ -94,19 +94,20 @@ def gpu_on_heads(inp, out, qk_heads=None):
     return res
 
 
-# Floor of a chunk's reference norm in the per-chunk error, as a fraction of the chunk's
-# share of the whole tensor's norm (sqrt(rows of the chunk / rows of the tensor) of it):
-# a chunk whose gradient is genuinely tiny is then judged against the tensor's scale
-# instead of its own, while a wrong row (about 1/8 of a 64-row chunk's norm) or a wrong
-# partial tail still counts against the chunk it sits in.
+# Floor of a chunk's reference norm in the per-chunk error, as a fraction of a full chunk's
+# share of the whole tensor's norm (sqrt(C / rows of the tensor) of it): a chunk whose
+# gradient is genuinely tiny, or a partial chunk of a token or two (whose "tensor" is a
+# handful of values, where bf16 rounding alone reaches ~2e-2), is then judged against the
+# scale of a chunk of this tensor instead of its own, while a wrong row (about 1/8 of a
+# 64-row chunk's norm) or a wrong partial tail still counts against the chunk it sits in.
 CHUNK_FLOOR = 0.25
 TOKEN_KEYS = ("dq", "dk", "dv", "dg", "dbeta", "o")
 
 
 def chunk_errors(x, ref, cu, C):
     """Per-(chunk, head) relative L2 errors of a token-major tensor [T, heads, ...] (fp64),
-    with the chunk reference norm floored as described at CHUNK_FLOOR. Returns an array
-    [chunks, heads]."""
+    chunks of C tokens within each sequence of cu, with the chunk reference norm floored as
+    described at CHUNK_FLOOR. Returns an array [chunks, heads]."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     T = ref.shape[0]
@@ -120,7 +121,7 @@ def chunk_errors(x, ref, cu, C):
             e = min(s + C, b)
             num = np.sqrt(np.sum((x[s:e] - ref[s:e]) ** 2, axis=(0, 2)))
             den = np.sqrt(np.sum(ref[s:e] ** 2, axis=(0, 2)))
-            floor = CHUNK_FLOOR * full * np.sqrt((e - s) / max(T, 1))
+            floor = CHUNK_FLOOR * full * np.sqrt(min(C, T) / max(T, 1))
             den = np.maximum(den, floor)
             out.append(np.where(den > 0, num / np.where(den > 0, den, 1.0), num))
     return np.array(out).reshape(-1, heads)
