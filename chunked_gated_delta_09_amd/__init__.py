@@ -11,7 +11,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["load", "fwd_states", "chunk_bwd", "chunk_bwd_into", "make_dims", "num_chunks",
+__all__ = ["load", "fwd_states", "chunk_bwd", "chunk_bwd_into", "chunk_bwd_noalloc_into", "make_dims", "num_chunks",
            "fwd_workspace_bytes", "bwd_workspace_bytes", "KdaError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -60,6 +60,8 @@ def load():
         lib.kda_fwd_states.argtypes = [dp] + [vp] * 10 + [vp, sz, vp]
         lib.kda_chunk_bwd.restype = ctypes.c_int
         lib.kda_chunk_bwd.argtypes = [dp] + [vp] * 15 + [vp, sz, vp]
+        lib.kda_chunk_bwd_noalloc.restype = ctypes.c_int
+        lib.kda_chunk_bwd_noalloc.argtypes = [dp] + [vp] * 15 + [vp]
         _lib = lib
     return _lib
 
@@ -177,6 +179,16 @@ def chunk_bwd_into(dims, q, k, v, g, beta, states, inv, dO, dS_final, dq, dk, dv
     _check(load().kda_chunk_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(states),
                                 _ptr(inv), _ptr(dO), _ptr(dS_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
                                 _ptr(dbeta), _ptr(dh0), _ptr(workspace), workspace.numel(), st))
+
+
+def chunk_bwd_noalloc_into(dims, q, k, v, g, beta, states, inv, dO, dS_final, dq, dk, dv, dg, dbeta, dh0,
+                           stream=None):
+    """kda_chunk_bwd_noalloc: as chunk_bwd_into with the library's own static workspace (at
+    most KDA_NOALLOC_MAX_WORKSPACE bytes; calls on one GPU must not overlap)."""
+    st = _stream() if stream is None else ctypes.c_void_p(stream)
+    _check(load().kda_chunk_bwd_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(states), _ptr(inv), _ptr(dO), _ptr(dS_final), _ptr(dq), _ptr(dk),
+                                        _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), st))
 
 
 def chunk_bwd(q, k, v, g, beta, states, inv, dO, dS_final=None, cu_seqlens=None, C=64, scale=None,

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["kda_api.cpp", "kda_fwd.hip", "kda_scan.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_fwd.hip", "kda_scan.hip", "kda_bwd.hip", "kda_noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled: plain float code is compiled to scalar VALU ops.

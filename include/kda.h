@@ -142,6 +142,24 @@ kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const void* k, con
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* kda_last_error(void);
 
+/*
+ * kda_chunk_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same computation and
+ * arguments without `workspace` / `ws_bytes`. The workspace is a device array inside the
+ * library, KDA_NOALLOC_MAX_WORKSPACE bytes per GPU, held from the library's load until the
+ * process ends; the call itself allocates nothing. A call whose kda_bwd_workspace_bytes
+ * exceeds that size returns KDA_EINVAL (before any HIP work). All calls on one GPU share
+ * its array, so calls that overlap on one GPU (different streams or threads) race: order
+ * them on one stream. Its first call on a device looks the array's address up on that
+ * device (which must be current, as for every call).
+ */
+#define KDA_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+kda_status kda_chunk_bwd_noalloc(const kda_dims* dims, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const void* states, const void* inv,
+                                 const void* dO, const void* dS_final,
+                                 void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                                 void* stream);
+
 
 #ifdef __cplusplus
 }
