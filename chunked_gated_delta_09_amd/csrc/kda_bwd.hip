@@ -17,7 +17,9 @@
 // bwd_prep_kernel writes what the reverse scan needs per chunk (kr, -w^T, e^gam and
 // W = (qd - Mqk w)^T dO, so that dS_in = diag(e^gam) dS + W - w^T (kr dS)); the scan then
 // leaves dS and kr dS per chunk; bwd_grad_kernel forms every gradient of one chunk with
-// all C x C triangles kept in LDS.
+// all C x C triangles kept in LDS. The triangle products take q, k referenced to R per
+// column and 16-row block (choose_refs in kda_device.h: R = 0 where |G| stays small), so
+// e^(G_i - G_j) never passes through an out-of-range e^(-G).
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -32,7 +34,7 @@ extern "C" __attribute__((visibility("default"))) int kda_phase_ts_read(void* ho
 
 // LDS plan of the bwd prep kernel, small enough for two workgroups per CU. Later buffers
 // overlay earlier ones that a barrier has retired:
-//   Qd, Ki (phases 0-2)            -> dO^T (phase 3)
+//   QL, KiL (phases 0-2: scale q e^(G - R), k e^(R - G), block-referenced) -> dO^T (phase 3)
 //   beta kd^T (phases 0-1a)        -> Q'^T (phases 2-3)
 //   INV (phases 0-1a)              -> Mqk (phases 1b-2)
 //   W^T (phases 1a-2)
@@ -50,8 +52,12 @@ struct BwdPrepLds {
   static constexpr size_t oMqk = oINV;
   static constexpr size_t oWT = oINV + sizeof(T) * C * LDC;
   static constexpr size_t oBeta = oWT + sizeof(T) * K * LDC;
-  static constexpr size_t total = oBeta + sizeof(float) * C;
-  static_assert(sizeof(T) * V * LDC <= oBKdT, "dO^T overlays Qd and Ki");
+  static constexpr size_t oRt = oBeta + sizeof(float) * C;  // R of each 16-row block per channel
+  static constexpr size_t oD = oRt + sizeof(float) * (C / 16) * K;  // ratios of consecutive R
+  static constexpr size_t oFlag = oD + sizeof(float) * (C / 16 - 1) * K;  // per-wave reference mode
+  static constexpr size_t total = oFlag + sizeof(int) * NW;
+  static_assert(sizeof(T) * V * LDC <= oBKdT, "dO^T overlays QL and KiL");
+  static_assert(C > 64 || total <= 80 * 1024, "two workgroups per CU");
 };
 
 // One workgroup per (chunk, value head); two fit on a CU (LDS plan above, at most 128
@@ -66,8 +72,11 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
   constexpr int NCK = (KT + NW - 1) / NW, NCV = (VT + NW - 1) / NW, NI = (C * C + NTH - 1) / NTH;
   constexpr int LDK = Lay::LDK, LDC = Lay::LDC;
   __shared__ __align__(16) unsigned char smem[Lay::total];
-  T* Qd = reinterpret_cast<T*>(smem + Lay::oQd);
-  T* Ki = reinterpret_cast<T*>(smem + Lay::oKi);
+  T* QL = reinterpret_cast<T*>(smem + Lay::oQd);
+  T* KiL = reinterpret_cast<T*>(smem + Lay::oKi);
+  float* Rt = reinterpret_cast<float*>(smem + Lay::oRt);
+  float* D = reinterpret_cast<float*>(smem + Lay::oD);
+  int* wflag = reinterpret_cast<int*>(smem + Lay::oFlag);
   T* BKdT = reinterpret_cast<T*>(smem + Lay::oBKdT);
   T* DoT = reinterpret_cast<T*>(smem + Lay::oDoT);
   T* INVt = reinterpret_cast<T*>(smem + Lay::oINV);
@@ -121,26 +130,33 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
   __syncthreads();
 
   // ---- gate cumsum and the decayed keys / queries
+  bool strong_w = false;  // this wave's columns take block references
 #pragma unroll
   for (int ci = 0; ci < NCK; ++ci) {
     const int kt = wave + ci * NW;
     if (kt < KT) {
       const int col = 16 * kt + n;
       const float gam = col_prefix<RT>(G[ci], lane);  // the column total is gam
+      float R[RT];
+      strong_w = choose_refs<RT>(G[ci], R, lane) || strong_w;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        f32x4 bk, qd4, ki4, kr4;
+        f32x4 bk, ql4, ki4, kr4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * rt + 4 * grp + j;
           const float e = __expf(G[ci][rt][j]);
-          qd4[j] = s.scale * qv[ci][rt][j] * e;
-          ki4[j] = kv[ci][rt][j] * __expf(-G[ci][rt][j]);
+          ql4[j] = s.scale * qv[ci][rt][j] * __expf(G[ci][rt][j] - R[rt]);
+          ki4[j] = kv[ci][rt][j] * __expf(R[rt] - G[ci][rt][j]);
           bk[j] = betas[row] * kv[ci][rt][j] * e;
           kr4[j] = kv[ci][rt][j] * __expf(gam - G[ci][rt][j]);
         }
-        store_rows<T>(Qd, LDK, 16 * rt, 16 * kt, qd4, lane, 1 << 30);
-        store_rows<T>(Ki, LDK, 16 * rt, 16 * kt, ki4, lane, 1 << 30);
+        if (grp == 0) {
+          Rt[rt * K + col] = R[rt];
+          if (rt + 1 < RT) D[rt * K + col] = __expf(R[rt + 1] - R[rt]);
+        }
+        store_rows<T>(QL, LDK, 16 * rt, 16 * kt, ql4, lane, 1 << 30);
+        store_rows<T>(KiL, LDK, 16 * rt, 16 * kt, ki4, lane, 1 << 30);
         if constexpr (sizeof(T) == 2) {
           // row layout (this lane: row 16rt + n, columns 16kt + 4grp ..): one 8-byte piece
           st4(krg + ScanFrag<K, V, C>::p1(16 * rt + n, 16 * kt + 4 * grp), to_rows_bf16(kr4[0], kr4[1], kr4[2], kr4[3], lane));
@@ -153,6 +169,7 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
       if (grp == 0) egc[col] = __expf(gam);
     }
   }
+  if (lane == 0) wflag[wave] = strong_w;
 #pragma unroll
   for (int i = 0; i < NIV; ++i) {
     const int pid = tid + i * NTH;
@@ -185,21 +202,22 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
         }
       }, wave, lane);
   __syncthreads();  // INV and beta kd^T retired
-  // Mqk = tril(qd ki^T), row-major.
-  block_gemm<T, RT, RT, 1, NW, K>(
-      Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
-      [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+  // Mqk = tril(qd ki^T), row-major, from the block-referenced q and keys.
+  const bool scl = any_flag<NW>(wflag);  // some column takes block references
+  tri_tiles<T, RT, NW, K>(
+      QL, LDK, KiL, LDK, D, K, scl,
+      [&](int mt, int nt0, f32x4 acc) {
         f32x4 m4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
-          m4[j] = col <= row ? acc[0][j] : 0.f;
+          m4[j] = col <= row ? acc[j] : 0.f;
         }
         store_rows<T>(Mqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
       }, wave, lane);
   __syncthreads();
   KDA_TS(0, 2);
-  // Q' = qd - Mqk w, transposed.
+  // Q' = qd - Mqk w, transposed (qd = QL e^R, rows of block mt).
   block_gemm<T, RT, KT, BNK, NW, C>(
       Mqk, LDC, 1 << 30, WT, LDC, [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
       [&](int, int mt, int nt0, f32x4(&acc)[BNK]) {
@@ -207,13 +225,14 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
         for (int jb = 0; jb < BNK; ++jb) {
           const int col = 16 * (nt0 + jb) + n;
           f32x4 qp4;
+          const float eR = scl ? __expf(Rt[mt * K + col]) : 1.f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) qp4[j] = to_f(Qd[(16 * mt + 4 * grp + j) * LDK + col]) - acc[jb][j];
+          for (int j = 0; j < 4; ++j) qp4[j] = to_f(QL[(16 * mt + 4 * grp + j) * LDK + col]) * eR - acc[jb][j];
           st4(QpT + col * LDC + 16 * mt + 4 * grp, qp4);
         }
       }, wave, lane);
-  __syncthreads();  // Qd, Ki, Mqk, W^T retired
-  // dO^T over Qd and Ki
+  __syncthreads();  // QL, KiL, Mqk, W^T retired
+  // dO^T over QL and KiL
 #pragma unroll
   for (int cv = 0; cv < NCV; ++cv) {
     const int vt = wave + cv * NW;
@@ -264,11 +283,14 @@ struct GradLds {
   static constexpr size_t endA = mx(3 * szCK + szVK, 3 * szKC + 2 * szCV);
   static constexpr size_t oVcT = endA, oDuT = endA;
   static constexpr size_t oINV = endA + szVC, oINVT = oINV + szCC;
-  static constexpr size_t oDMqk = endA, oDMqkT = endA + szCC, oDL = endA + 2 * szCC, oBDLT = endA + 3 * szCC;
+  static constexpr size_t oDMqk = endA, oDMqkT = endA + szCC, oDL = endA + 2 * szCC, oDLT = endA + 3 * szCC;
   static constexpr size_t endB = mx(endA + szVC + 2 * szCC, endA + 4 * szCC);
   static constexpr size_t oMqkT = endB;
   static constexpr size_t oBeta = oMqkT + szCC;
-  static constexpr size_t oDbp = oBeta + sizeof(float) * C;
+  static constexpr size_t oRt = oBeta + sizeof(float) * C;  // R of each 16-row block per channel
+  static constexpr size_t oD = oRt + sizeof(float) * (C / 16) * K;  // ratios of consecutive R
+  static constexpr size_t oFlag = oD + sizeof(float) * (C / 16 - 1) * K;  // per-wave reference mode
+  static constexpr size_t oDbp = oFlag + sizeof(int) * NW;
   static constexpr size_t oDoT = oDbp + sizeof(float) * 2 * NW * C;  // dbeta partials: dvc part, then phase-3 part
   // dg leaves through the dO slot in passes of SR rows of K fp32 (row stride K + 4)
   static constexpr int SR = C < 32 ? C : 32;
@@ -302,13 +324,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
   constexpr int NITC = (RT * RT + NW - 1) / NW;
   constexpr int NKV = V / M::KS;
   __shared__ __align__(16) unsigned char smem[Lay::total];
-  T* Qd = reinterpret_cast<T*>(smem + Lay::oQd);
+  T* QL = reinterpret_cast<T*>(smem + Lay::oQd);
   T* Kd = reinterpret_cast<T*>(smem + Lay::oKd);
-  T* Ki = reinterpret_cast<T*>(smem + Lay::oKi);
+  T* KiL = reinterpret_cast<T*>(smem + Lay::oKi);
   T* SinT = reinterpret_cast<T*>(smem + Lay::oSinT);
-  T* QdT = reinterpret_cast<T*>(smem + Lay::oQdT);
-  T* KdT = reinterpret_cast<T*>(smem + Lay::oKdT);
-  T* KiT = reinterpret_cast<T*>(smem + Lay::oKiT);
+  T* QLT = reinterpret_cast<T*>(smem + Lay::oQdT);
+  T* BKLT = reinterpret_cast<T*>(smem + Lay::oKdT);
+  T* KiLT = reinterpret_cast<T*>(smem + Lay::oKiT);
   T* U = reinterpret_cast<T*>(smem + Lay::oU);
   T* Ndv = reinterpret_cast<T*>(smem + Lay::oNdv);
   T* VcT = reinterpret_cast<T*>(smem + Lay::oVcT);
@@ -318,9 +340,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
   T* DMqk = reinterpret_cast<T*>(smem + Lay::oDMqk);
   T* DMqkT = reinterpret_cast<T*>(smem + Lay::oDMqkT);
   T* DL = reinterpret_cast<T*>(smem + Lay::oDL);
-  T* BDLT = reinterpret_cast<T*>(smem + Lay::oBDLT);
+  T* DLT = reinterpret_cast<T*>(smem + Lay::oDLT);
   T* MqkT = reinterpret_cast<T*>(smem + Lay::oMqkT);
   float* betas = reinterpret_cast<float*>(smem + Lay::oBeta);
+  float* Rt = reinterpret_cast<float*>(smem + Lay::oRt);
+  float* D = reinterpret_cast<float*>(smem + Lay::oD);
+  int* wflag = reinterpret_cast<int*>(smem + Lay::oFlag);
   float* dbpart = reinterpret_cast<float*>(smem + Lay::oDbp);
   T* DoT = reinterpret_cast<T*>(smem + Lay::oDoT);  // dO^T, then dO row-major (same slot)
   T* DoR = DoT;
@@ -465,7 +490,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     }
 
     // ---- phase 1 compute: column tiles of g, q, k and v into the column-owner layout; gate
-    // cumsum, decayed q/k (row-major), S_in^T
+    // cumsum, block references R, block-referenced q and keys and decayed keys (row-major),
+    // S_in^T
     if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
@@ -488,40 +514,54 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       }
     }
     float gam[NCT];
+    bool strong_c[NCT];  // column tile ci takes block references
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
       const int kt = wave + ci * NW;
       gam[ci] = 0.f;
+      strong_c[ci] = false;
       if (kt < KT) {
         const int col = 16 * kt + n;
         gam[ci] = col_prefix<RT>(Gr[ci], lane);  // the column total is gam
+        float R[RT];
+        strong_c[ci] = choose_refs<RT>(Gr[ci], R, lane);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           f32x4 q4, kd4, ki4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float eG = __expf(Gr[ci][rt][j]);
-            q4[j] = s.scale * qv[ci][rt][j] * eG;
-            kd4[j] = kv[ci][rt][j] * eG;
-            ki4[j] = kv[ci][rt][j] * __expf(-Gr[ci][rt][j]);
+            const float G = Gr[ci][rt][j];
+            q4[j] = s.scale * qv[ci][rt][j] * __expf(G - R[rt]);
+            kd4[j] = kv[ci][rt][j] * __expf(G);
+            ki4[j] = kv[ci][rt][j] * __expf(R[rt] - G);
+          }
+          if (grp == 0) {
+            Rt[rt * K + col] = R[rt];
+            if (rt + 1 < RT) D[rt * K + col] = __expf(R[rt + 1] - R[rt]);
           }
           if constexpr (sizeof(T) == 2) {
             // row layout (this lane: row 16rt + n, columns 16kt + 4grp ..): 8-byte writes
             const int off = (16 * rt + n) * LDK + 16 * kt + 4 * grp;
-            st4(Qd + off, to_rows_bf16(q4[0], q4[1], q4[2], q4[3], lane));
+            st4(QL + off, to_rows_bf16(q4[0], q4[1], q4[2], q4[3], lane));
             st4(Kd + off, to_rows_bf16(kd4[0], kd4[1], kd4[2], kd4[3], lane));
-            st4(Ki + off, to_rows_bf16(ki4[0], ki4[1], ki4[2], ki4[3], lane));
+            st4(KiL + off, to_rows_bf16(ki4[0], ki4[1], ki4[2], ki4[3], lane));
           } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int row = 16 * rt + 4 * grp + j;
-              Qd[row * LDK + col] = from_f<T>(q4[j]);
+              QL[row * LDK + col] = from_f<T>(q4[j]);
               Kd[row * LDK + col] = from_f<T>(kd4[j]);
-              Ki[row * LDK + col] = from_f<T>(ki4[j]);
+              KiL[row * LDK + col] = from_f<T>(ki4[j]);
             }
           }
         }
       }
+    }
+    {
+      int f = 0;
+#pragma unroll
+      for (int ci = 0; ci < NCT; ++ci) f |= strong_c[ci];
+      if (lane == 0) wflag[wave] = f;
     }
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
@@ -568,13 +608,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       }
     }
 
-    // ---- Mqk = tril(qd ki^T) -> Mqk^T; F = kd ki^T (registers, same tile walk as dL below)
-    block_gemm<T, RT, RT, 1, NW, K>(
-        Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
-        [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+    // ---- Mqk = tril(qd ki^T) -> Mqk^T, from the block-referenced q and keys
+    tri_tiles<T, RT, NW, K>(
+        QL, LDK, KiL, LDK, D, K, any_flag<NW>(wflag),
+        [&](int mt, int nt0, f32x4 acc) {
           f32x4 m4;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) m4[j] = (16 * nt0 + n <= 16 * mt + 4 * grp + j) ? acc[0][j] : 0.f;
+          for (int j = 0; j < 4; ++j) m4[j] = (16 * nt0 + n <= 16 * mt + 4 * grp + j) ? acc[j] : 0.f;
           st4(MqkT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, m4);
         }, wave, lane);
     // ---- kd S_in -> vcorr^T = (beta (v - kd S_in))^T
@@ -596,25 +636,36 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     __syncthreads();
 
     KDA_TS(2, 2);
-    // ---- qd^T, kd^T, ki^T (region A, over the dead Qd/Kd/Ki/S_in^T); dO^T
+    // ---- block-referenced q^T, (beta k)^T (decayed) and k^T (inverse decay), region A over
+    // the dead QL/Kd/KiL/S_in^T; dO^T
 #pragma unroll
     for (int ci = 0; ci < NCT; ++ci) {
       const int kt = wave + ci * NW;
       if (kt < KT) {
         const int col = 16 * kt + n;
+        // LDS reads first: a read issued after the stores below would wait for them
+        f32x4 b4s[RT];
+        float Rs[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
+          b4s[rt] = *reinterpret_cast<const f32x4*>(betas + 16 * rt + 4 * grp);
+          Rs[rt] = strong_c[ci] ? Rt[rt * K + col] : 0.f;
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float Rr = Rs[rt];
+          const f32x4 b4 = b4s[rt];
           f32x4 q4, kd4, ki4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float eG = __expf(Gr[ci][rt][j]);
-            q4[j] = s.scale * qv[ci][rt][j] * eG;
-            kd4[j] = kv[ci][rt][j] * eG;
-            ki4[j] = kv[ci][rt][j] * __expf(-Gr[ci][rt][j]);
+            const float eGR = __expf(Gr[ci][rt][j] - Rr);
+            q4[j] = s.scale * qv[ci][rt][j] * eGR;
+            kd4[j] = b4[j] * (kv[ci][rt][j] * eGR);
+            ki4[j] = kv[ci][rt][j] * __expf(Rr - Gr[ci][rt][j]);
           }
-          st4(QdT + col * LDC + 16 * rt + 4 * grp, q4);
-          st4(KdT + col * LDC + 16 * rt + 4 * grp, kd4);
-          st4(KiT + col * LDC + 16 * rt + 4 * grp, ki4);
+          st4(QLT + col * LDC + 16 * rt + 4 * grp, q4);
+          st4(BKLT + col * LDC + 16 * rt + 4 * grp, kd4);
+          st4(KiLT + col * LDC + 16 * rt + 4 * grp, ki4);
         }
       }
     }
@@ -754,18 +805,17 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
               al = M::mma(fn[k], fu[k], al);
             }
           }
-          f32x4 m4, l4, b4;
+          f32x4 m4, l4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
             m4[j] = col <= row ? am[j] : 0.f;
             l4[j] = col < row ? al[j] : 0.f;
-            b4[j] = betas[row] * l4[j];
           }
           store_rows<T>(DMqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
           st4(DMqkT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, m4);
           store_rows<T>(DL, LDC, 16 * mt, 16 * nt0, l4, lane, 1 << 30);
-          st4(BDLT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, b4);
+          st4(DLT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, l4);
         }
       }
     }
@@ -791,20 +841,41 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         f32x4 aq[RT], akd[RT], ai[RT], ar[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) aq[rt] = akd[rt] = ai[rt] = ar[rt] = zero4();
-        // triangle products first (LDS only), while the S_in / dS fragments arrive
+        // ai = dMqk^T qd + dL^T diag(beta) kd relative to R_rt (LDS only: runs while the S_in /
+        // dS fragments arrive). Each lane's contraction values lie in one 16-row block blk;
+        // the rows of blocks after rt take e^(R_blk - R_rt) <= 1.
+        float Rc[RT];  // block references of this lane's column
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) Rc[rt] = strong_c[ci] ? Rt[rt * K + col] : 0.f;
+        // this lane's contraction values at step kk lie in block kk/16 (lane groups whose
+        // offset PER grp stays below 16) or kk/16 + 1: the reference of its block, clamped
+        // to [lo, hi] (indices known at compile time once the loops are unrolled)
+        auto pick = [&](int b) {  // Rc[b] as a select chain (no dynamic register indexing)
+          float r = Rc[0];
+#pragma unroll
+          for (int i = 1; i < RT; ++i) r = b == i ? Rc[i] : r;
+          return r;
+        };
+        auto ref_of = [&](int kk, int lo, int hi) {
+          const int b0 = min(max(kk >> 4, lo), hi), b1 = min(max((kk + M::KS - 1) >> 4, lo), hi);
+          float r0 = pick(b0), r1 = pick(b1);
+          asm volatile("" : "+v"(r0), "+v"(r1));  // a select of values, not of array slots
+          return ((kk & 15) + M::PER * grp >= 16) ? r1 : r0;
+        };
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const int klo = min(C, round_up<T>(16 * (rt + 1)));
-          for (int kk = 0; kk < klo; kk += M::KS) {
-            const typename M::frag b = frag_ld<T>(KiT, LDC, 16 * kt, kk, lane, C, 1 << 30);
-            aq[rt] = M::mma(frag_ld<T>(DMqk, LDC, 16 * rt, kk, lane, C, 1 << 30), b, aq[rt]);
-            akd[rt] = M::mma(frag_ld<T>(DL, LDC, 16 * rt, kk, lane, C, 1 << 30), b, akd[rt]);
-          }
+          const float Rr = Rc[rt];
+#pragma unroll
           for (int kk = round_dn<T>(16 * rt); kk < C; kk += M::KS) {
-            ai[rt] = M::mma(frag_ld<T>(DMqkT, LDC, 16 * rt, kk, lane, C, 1 << 30),
-                            frag_ld<T>(QdT, LDC, 16 * kt, kk, lane, C, 1 << 30), ai[rt]);
-            ai[rt] = M::mma(frag_ld<T>(BDLT, LDC, 16 * rt, kk, lane, C, 1 << 30),
-                            frag_ld<T>(KdT, LDC, 16 * kt, kk, lane, C, 1 << 30), ai[rt]);
+            typename M::frag bq = frag_ld<T>(QLT, LDC, 16 * kt, kk, lane, C, 1 << 30);
+            typename M::frag bk = frag_ld<T>(BKLT, LDC, 16 * kt, kk, lane, C, 1 << 30);
+            if (strong_c[ci] && kk + M::KS > 16 * (rt + 1)) {
+              const float f = __expf(ref_of(kk, rt, RT - 1) - Rr);
+              bq = scale_frag<T>(bq, f);
+              bk = scale_frag<T>(bk, f);
+            }
+            ai[rt] = M::mma(frag_ld<T>(DMqkT, LDC, 16 * rt, kk, lane, C, 1 << 30), bq, ai[rt]);
+            ai[rt] = M::mma(frag_ld<T>(DLT, LDC, 16 * rt, kk, lane, C, 1 << 30), bk, ai[rt]);
           }
         }
         float rsum = 0.f;  // this lane's share of sum_v dS[k][v] S_in[k][v], k = col
@@ -833,6 +904,29 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
           }
         }
         rsum = col_allsum(rsum);
+        // aq, akd relative to R_rt: with block references the state terms above take the
+        // factor e^(R_rt) (to 0 where it underflows: their true size is below fp32's range);
+        // then the triangle products dMqk ki, dL ki, the keys of blocks before rt taking
+        // e^(R_rt - R_blk) <= 1
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          if (strong_c[ci]) {
+            const float eR = __expf(Rc[rt]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              aq[rt][j] *= eR;
+              akd[rt][j] *= eR;
+            }
+          }
+          const int klo = min(C, round_up<T>(16 * (rt + 1)));
+#pragma unroll
+          for (int kk = 0; kk < klo; kk += M::KS) {
+            typename M::frag b = frag_ld<T>(KiLT, LDC, 16 * kt, kk, lane, C, 1 << 30);
+            if (strong_c[ci] && kk < 16 * rt) b = scale_frag<T>(b, __expf(Rc[rt] - ref_of(kk, 0, rt)));
+            aq[rt] = M::mma(frag_ld<T>(DMqk, LDC, 16 * rt, kk, lane, C, 1 << 30), b, aq[rt]);
+            akd[rt] = M::mma(frag_ld<T>(DL, LDC, 16 * rt, kk, lane, C, 1 << 30), b, akd[rt]);
+          }
+        }
         const float g_last = gam[ci];
         float dG[RT][4];
         float krd = 0.f;
@@ -840,22 +934,35 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         for (int rt = 0; rt < RT; ++rt) {
           float dbz[4];
           f32x4 dq4, dk4;
+          const float Rr = Rc[rt];
+          // dG = q dq + k (dk_d - dk_i - dk_r), its triangle terms taken as the row factors
+          // times aq, akd, ai with the factors as rounded into the MFMA operands (read back
+          // from them: this lane's 4 rows of its column). A pair (i, j) of the diagonal block
+          // then enters dG_i and dG_j as the same product of the same values and cancels in
+          // the chunk's reverse cumsum to fp32 precision; under strong decay most of dG is
+          // such pairs, and the fp32 factors would leave bf16-sized residues.
+          typedef T t4r __attribute__((ext_vector_type(4)));
+          const t4r qlr = *reinterpret_cast<const t4r*>(QLT + col * LDC + 16 * rt + 4 * grp);
+          const t4r bklr = *reinterpret_cast<const t4r*>(BKLT + col * LDC + 16 * rt + 4 * grp);
+          const t4r kilr = *reinterpret_cast<const t4r*>(KiLT + col * LDC + 16 * rt + 4 * grp);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * rt + 4 * grp + j;
             const float G = Gr[ci][rt][j];
-            const float eG = __expf(G), emG = __expf(-G), erG = __expf(g_last - G);
-            const float dq_e = s.scale * eG * aq[rt][j];
-            const float dk_d = eG * betas[row] * akd[rt][j], dk_i = emG * ai[rt][j], dk_r = erG * ar[rt][j];
+            const float eGR = __expf(G - Rr), eRG = __expf(Rr - G), erG = __expf(g_last - G);
+            const float kl = kv[ci][rt][j] * eGR;
+            dG[rt][j] = to_f(qlr[j]) * aq[rt][j] + to_f(bklr[j]) * akd[rt][j] - to_f(kilr[j]) * ai[rt][j];
+            const float dq_e = s.scale * eGR * aq[rt][j];
+            const float dk_d = eGR * betas[row] * akd[rt][j], dk_i = eRG * ai[rt][j], dk_r = erG * ar[rt][j];
             dq4[j] = dq_e;
             dk4[j] = dk_d + dk_i + dk_r;
             if constexpr (GVA) {
               dqa[ci][rt][j] += dq_e;
               dka[ci][rt][j] += dk4[j];
             }
-            dG[rt][j] = qv[ci][rt][j] * dq_e + kv[ci][rt][j] * (dk_d - dk_i - dk_r);
+            dG[rt][j] -= kv[ci][rt][j] * dk_r;
             krd += kv[ci][rt][j] * dk_r;
-            dbz[j] = kv[ci][rt][j] * eG * akd[rt][j];  // dbeta part 2: rowsum(kd o akd)
+            dbz[j] = kl * akd[rt][j];  // dbeta part 2: rowsum(kd o akd)
           }
           if constexpr (!GVA) {
             store_rows<T>(dqc, qs, 16 * rt, 16 * kt, dq4, lane, len);

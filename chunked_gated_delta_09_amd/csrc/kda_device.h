@@ -72,6 +72,9 @@ __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
 template <class T>
 __device__ __forceinline__ T from_f(float x) { return (T)x; }
+// x rounded to T and back (the value an operand of type T holds)
+template <class T>
+__device__ __forceinline__ float rnd(float x) { return to_f(from_f<T>(x)); }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -532,6 +535,149 @@ struct ScanCols {
   __device__ __forceinline__ static int slice(int v) { return 2 * (v >> 5) + ((v & 7) >> 2); }
   __device__ __forceinline__ static int lane_col(int v) { return 4 * ((v & 31) >> 3) + (v & 3); }
 };
+
+// ---------------------------------------------------------------------------------
+// Sub-block reference points of the intra-chunk gate factors. A chunk's rows are taken in
+// blocks of 16, with R_b the chunk-local cumsum G at block b's first row (G is
+// non-increasing while g <= 0). For i in block a and j in block b <= a,
+//   e^(G_i - G_j) = e^(G_i - R_a) * e^(R_a - R_b) * e^(R_b - G_j),
+// with e^(G_i - R_a) <= 1, e^(R_a - R_b) <= 1 and 1 <= e^(R_b - G_j) <= e^(15 max|g|): no
+// factor leaves the fp32 / bf16 range however strong the decay across the whole chunk,
+// whereas e^(G_i) and e^(-G_j) taken apart overflow once a chunk's G drops below about -87
+// (the FLA chunk_kda_bwd page passes this as its safe_gate mode: sub-chunk reference
+// points). The kernels keep block-referenced rows (a e^(G - R), k e^(R - G)) and apply the
+// middle factor to one operand of each tile below the diagonal block.
+// ---------------------------------------------------------------------------------
+
+// R of every row tile for this lane's column, from its column-owner cumsum x[rt][j] (rows
+// 16rt + 4grp + j): row 16rt is held by lane group 0, slot 0; broadcast over the lane groups.
+template <int RT>
+__device__ __forceinline__ void block_refs(const float (&x)[RT][4], float (&R)[RT], int lane) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+    R[rt] = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) << 2, __float_as_int(x[rt][0])));
+}
+
+// The kernels choose the references per wave (per 16-column tile of a chunk-head): where
+// every |G| of the wave's columns is at most kMildG, R = 0 for every block (the chunk-start
+// reference: e^(+-G) themselves are in range and no operand needs the middle factor, which
+// is then exactly 1); otherwise R = the block references above. Any R gives the same
+// products. Returns whether block references were taken (wave-uniform).
+constexpr float kMildG = 80.f;
+template <int RT>
+__device__ __forceinline__ bool choose_refs(const float (&x)[RT][4], float (&R)[RT], int lane) {
+  bool big = false;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) big = big || !(fabsf(x[rt][j]) <= kMildG);
+  const bool strong = __builtin_amdgcn_ballot_w64(big) != 0;
+  if (strong) {
+    block_refs<RT>(x, R, lane);
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) R[rt] = 0.f;
+  }
+  return strong;
+}
+
+// OR of the NW per-wave flags in LDS, as a wave-uniform value.
+template <int NW>
+__device__ __forceinline__ bool any_flag(const int* f) {
+  int a = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) a |= f[i];
+  return __builtin_amdgcn_readfirstlane(a) != 0;
+}
+
+// Scales the PER contraction values of a fragment by e^(R_a - R_b) of their channels
+// k0 .. k0 + PER - 1, b < a, as the product of the consecutive block ratios
+// D[c][k] = e^(R_(c+1)[k] - R_c[k]) for c = b .. a-1 (fp32 [RT-1][ldd]; each ratio <= 1).
+template <class T>
+__device__ __forceinline__ typename Mma<T>::frag scale_channels(typename Mma<T>::frag f, const float* D, int ldd,
+                                                                 int a, int b, int k0) {
+  if constexpr (sizeof(T) == 2) {
+    f32x4 x0 = *reinterpret_cast<const f32x4*>(D + b * ldd + k0);
+    f32x4 x1 = *reinterpret_cast<const f32x4*>(D + b * ldd + k0 + 4);
+    for (int c = b + 1; c < a; ++c) {
+      const f32x4 y0 = *reinterpret_cast<const f32x4*>(D + c * ldd + k0);
+      const f32x4 y1 = *reinterpret_cast<const f32x4*>(D + c * ldd + k0 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x0[i] *= y0[i];
+        x1[i] *= y1[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = (bf16)((float)f[i] * x0[i]);
+      f[4 + i] = (bf16)((float)f[4 + i] * x1[i]);
+    }
+    return f;
+  } else {
+    float x = D[b * ldd + k0];
+    for (int c = b + 1; c < a; ++c) x *= D[c * ldd + k0];
+    return f * x;
+  }
+}
+
+// A fragment times one fp32 factor (bf16: rounded back to bf16).
+template <class T>
+__device__ __forceinline__ typename Mma<T>::frag scale_frag(typename Mma<T>::frag f, float x) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (bf16)((float)f[i] * x);
+    return f;
+  } else {
+    return f * x;
+  }
+}
+
+// Lower-triangular C x C products over the channels with block-referenced operands:
+// tile (mt, nt), nt <= mt, of A Bt^T, where A holds rows a_i e^(G_i - R) and Bt rows
+// b_j e^(R - G_j) (row-major, contraction contiguous) and the Bt fragments of tiles below the
+// diagonal are scaled by e^(R_mt - R_nt) per channel (from the block ratios D, as in
+// scale_channels). Every RT x RT tile is dealt to the NW waves round-robin (as block_gemm
+// with BN = 1) and passed to epi(mt, nt, acc); tiles above the diagonal pass zero. scale:
+// whether any channel takes block references (else the middle factors are all 1). BATCH:
+// request every fragment of a tile before its first product (overlapping the LDS round
+// trips, at 8 more VGPRs per contraction step).
+template <class T, int RT, int NW, int KC, bool BATCH = true, class EPI>
+__device__ __forceinline__ void tri_tiles(const T* A, int lda, const T* Bt, int ldb, const float* D, int ldd, bool scale,
+                                          EPI epi, int wave, int lane) {
+  typedef Mma<T> M;
+  constexpr int NB = RT * RT, NIT = (NB + NW - 1) / NW, NK = KC / M::KS;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int blk = wave + it * NW;
+    if (blk < NB) {
+      const int mt = blk / RT, nt = blk % RT;
+      f32x4 acc = zero4();
+      if (nt <= mt && !BATCH) {
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          typename M::frag b = frag_ld<T>(Bt, ldb, 16 * nt, k * M::KS, lane);
+          if (scale && nt < mt) b = scale_channels<T>(b, D, ldd, mt, nt, k * M::KS + M::PER * (lane >> 4));
+          acc = M::mma(frag_ld<T>(A, lda, 16 * mt, k * M::KS, lane), b, acc);
+        }
+      } else if (nt <= mt) {
+        typename M::frag a[NK], b[NK];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          a[k] = frag_ld<T>(A, lda, 16 * mt, k * M::KS, lane);
+          b[k] = frag_ld<T>(Bt, ldb, 16 * nt, k * M::KS, lane);
+        }
+        if (scale && nt < mt) {
+#pragma unroll
+          for (int k = 0; k < NK; ++k) b[k] = scale_channels<T>(b[k], D, ldd, mt, nt, k * M::KS + M::PER * (lane >> 4));
+        }
+#pragma unroll
+        for (int k = 0; k < NK; ++k) acc = M::mma(a[k], b[k], acc);
+      }
+      epi(mt, nt, acc);
+    }
+  }
+}
 
 // Contraction-range helpers for triangular operands (K step = KS, tiles of 16 rows).
 template <class T>

@@ -7,6 +7,10 @@
 //   kd = k e^G, ki = k e^-G, kr = k e^(gam-G), qd = scale q e^G,
 //   INV = (I + strict_tril(diag(beta) kd ki^T))^-1,  w = INV diag(beta) kd,  u = INV diag(beta) v,
 //   U = u - w S_in,  S_out = diag(e^gam) S_in + kr^T U,  o = qd S_in + tril(qd ki^T) U.
+// The triangles kd ki^T and qd ki^T are formed from referenced rows (k e^(G - R), k e^(R - G),
+// scale q e^(G - R)): R = 0 for the columns whose |G| stays small, else the cumsum at the first
+// row of each 16-row block, so that every operand stays in range whatever the gates
+// (choose_refs, tri_tiles in kda_device.h).
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -44,9 +48,9 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
 
 // LDS plan of the forward prep kernel (two workgroups per CU). Later buffers overlay
 // earlier ones that a barrier has retired:
-//   Kd, Ki (until L)                 -> X (fp32 inverse) and INV (bf16 / fp32 operand)
+//   KL, KiL (until L)                -> X (fp32 inverse) and INV (bf16 / fp32 operand)
 //   L (fp32, until the inverse)      -> diag(beta) v^T
-//   diag(beta) kd^T (whole kernel)
+//   diag(beta) kd^T (whole kernel); R of each 16-row block per channel (until L)
 template <class T, int K, int V, int C>
 struct FwdPrepLds {
   static constexpr int P = pad_of<T>();
@@ -61,7 +65,9 @@ struct FwdPrepLds {
   static constexpr size_t oL = oBKdT + sizeof(T) * K * LDC;
   static constexpr size_t oBVT = oL;
   static constexpr size_t oBeta = oL + mx(sizeof(float) * C * LDL, sizeof(T) * V * LDC);
-  static constexpr size_t total = oBeta + sizeof(float) * C;
+  static constexpr size_t oD = oBeta + sizeof(float) * C;  // ratios of consecutive block references
+  static constexpr size_t oFlag = oD + sizeof(float) * (C / 16 - 1) * K;  // per-wave reference mode
+  static constexpr size_t total = oFlag + sizeof(int) * 8;
   static_assert(total <= 80 * 1024 || C > 64, "two workgroups per CU");
 };
 
@@ -129,11 +135,14 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
                                                            T* __restrict__ invp, FwdWs ws) {
   typedef FwdPrepLds<T, K, V, C> Lay;
   constexpr int NW = 8, RT = C / 16, KT = K / 16, VT = V / 16;
+  static_assert(NW <= 8, "one reference-mode flag per wave");
   constexpr int NCK = (KT + NW - 1) / NW, NCV = (VT + NW - 1) / NW;
   constexpr int LDK = Lay::LDK, LDC = Lay::LDC, LDL = Lay::LDL;
   __shared__ __align__(16) unsigned char smem[Lay::total];
-  T* Kd = reinterpret_cast<T*>(smem + Lay::oKd);
-  T* Ki = reinterpret_cast<T*>(smem + Lay::oKi);
+  T* KL = reinterpret_cast<T*>(smem + Lay::oKd);   // k e^(G - R), row-major
+  T* KiL = reinterpret_cast<T*>(smem + Lay::oKi);  // k e^(R - G), row-major
+  float* D = reinterpret_cast<float*>(smem + Lay::oD);
+  int* wflag = reinterpret_cast<int*>(smem + Lay::oFlag);
   float* Xf = reinterpret_cast<float*>(smem + Lay::oX);
   T* INVt = reinterpret_cast<T*>(smem + Lay::oINV);
   T* BKdT = reinterpret_cast<T*>(smem + Lay::oBKdT);
@@ -173,8 +182,10 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
   if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
   __syncthreads();
 
-  // ---- gate cumsum; kd, ki (row-major), diag(beta) kd^T, kr (scan fragment order), e^gam
+  // ---- gate cumsum; block-referenced keys (row-major), diag(beta) kd^T, kr (scan fragment
+  // order), e^gam
   T* __restrict__ krT = reinterpret_cast<T*>(ws.krT) + ch * (sizeof(T) == 2 ? ScanFrag<K, V, C>::P2_ELEMS : K * C);
+  bool strong_w = false;  // this wave's columns take block references
 #pragma unroll
   for (int ci = 0; ci < NCK; ++ci) {
     const int kt = wave + ci * NW;
@@ -184,20 +195,23 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
       tk[ci].get(kv, lane, len);
       const int col = 16 * kt + n;
       const float gam = col_prefix<RT>(G, lane);  // the column total is gam
+      float R[RT];
+      strong_w = choose_refs<RT>(G, R, lane) || strong_w;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        f32x4 kd4, ki4, bk, kr4;
+        f32x4 kd4, kl4, ki4, bk, kr4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * rt + 4 * grp + j;
-          const float e = __expf(G[rt][j]);
-          kd4[j] = kv[rt][j] * e;
-          ki4[j] = kv[rt][j] * __expf(-G[rt][j]);
+          kd4[j] = kv[rt][j] * __expf(G[rt][j]);
+          kl4[j] = kv[rt][j] * __expf(G[rt][j] - R[rt]);
+          ki4[j] = kv[rt][j] * __expf(R[rt] - G[rt][j]);
           bk[j] = betas[row] * kd4[j];
           kr4[j] = kv[rt][j] * __expf(gam - G[rt][j]);
         }
-        store_rows<T>(Kd, LDK, 16 * rt, 16 * kt, kd4, lane, 1 << 30);
-        store_rows<T>(Ki, LDK, 16 * rt, 16 * kt, ki4, lane, 1 << 30);
+        if (grp == 0 && rt + 1 < RT) D[rt * K + col] = __expf(R[rt + 1] - R[rt]);
+        store_rows<T>(KL, LDK, 16 * rt, 16 * kt, kl4, lane, 1 << 30);
+        store_rows<T>(KiL, LDK, 16 * rt, 16 * kt, ki4, lane, 1 << 30);
         st4(BKdT + col * LDC + 16 * rt + 4 * grp, bk);
         if constexpr (sizeof(T) == 2) {
           st4(krT + ScanFrag<K, V, C>::p2(col, 16 * rt + 4 * grp), kr4);
@@ -208,6 +222,7 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
       if (grp == 0) ws.eg[ch * K + col] = __expf(gam);
     }
   }
+  if (lane == 0) wflag[wave] = strong_w;
   float bv[NCV][RT][4];  // diag(beta) v in the column-owner layout, stored once L is retired
 #pragma unroll
   for (int cv = 0; cv < NCV; ++cv) {
@@ -219,17 +234,17 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
   }
   __syncthreads();
 
-  // ---- L = strict_tril(diag(beta) kd ki^T), fp32
-  block_gemm<T, RT, RT, 1, NW, K>(
-      Kd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
-      [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+  // ---- L = strict_tril(diag(beta) kd ki^T), fp32, from the block-referenced keys
+  tri_tiles<T, RT, NW, K, false>(
+      KL, LDK, KiL, LDK, D, K, any_flag<NW>(wflag),
+      [&](int mt, int nt0, f32x4 acc) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * mt + 4 * grp + j, col = 16 * nt0 + n;
-          Lf[row * LDL + col] = col < row ? betas[row] * acc[0][j] : 0.f;
+          Lf[row * LDL + col] = col < row ? betas[row] * acc[j] : 0.f;
         }
       }, wave, lane);
-  __syncthreads();  // Kd, Ki retired (the epilogue also wrote the skipped upper blocks as zero)
+  __syncthreads();  // KL, KiL retired (the epilogue also wrote the upper blocks as zero)
 
   // ---- INV = (I + L)^-1 (fp32, into the Kd/Ki region)
   unit_lower_inverse<C, NW>(Lf, Xf, LDL, wave, lane);
@@ -296,7 +311,10 @@ struct FwdOutLds {
   static constexpr size_t oMqk = oVcT + sizeof(T) * V * LDC;
   static constexpr size_t oUT = oMqk + sizeof(T) * C * LDC;
   static constexpr size_t oBeta = oUT + sizeof(T) * V * LDC;
-  static constexpr size_t total = oBeta + sizeof(float) * C;
+  static constexpr size_t oQL = oBeta + sizeof(float) * C;
+  static constexpr size_t oD = oQL + sizeof(T) * C * LDK;  // ratios of consecutive block references
+  static constexpr size_t oFlag = oD + sizeof(float) * (C / 16 - 1) * K;  // per-wave reference mode
+  static constexpr size_t total = oFlag + sizeof(int) * 8;
   static_assert(total <= 160 * 1024, "output kernel exceeds the LDS of one CU");
 };
 
@@ -313,6 +331,7 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
   typedef T vecT __attribute__((ext_vector_type(16 / sizeof(T))));
   typedef T t4 __attribute__((ext_vector_type(4)));
   constexpr int NW = 8, NTH = 64 * NW, RT = C / 16, KT = K / 16, VT = V / 16;
+  static_assert(NW <= 8, "one reference-mode flag per wave");
   constexpr int NCK = (KT + NW - 1) / NW;
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int LDK = Lay::LDK, LDC = Lay::LDC;
@@ -321,7 +340,10 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
   __shared__ __align__(16) unsigned char smem[Lay::total];
   T* Qd = reinterpret_cast<T*>(smem + Lay::oQd);
   T* Kd = reinterpret_cast<T*>(smem + Lay::oKd);
-  T* Ki = reinterpret_cast<T*>(smem + Lay::oKi);
+  T* KiL = reinterpret_cast<T*>(smem + Lay::oKi);  // k e^(R - G)
+  T* QL = reinterpret_cast<T*>(smem + Lay::oQL);   // scale q e^(G - R)
+  float* D = reinterpret_cast<float*>(smem + Lay::oD);
+  int* wflag = reinterpret_cast<int*>(smem + Lay::oFlag);
   T* SinT = reinterpret_cast<T*>(smem + Lay::oSinT);
   T* INVt = reinterpret_cast<T*>(smem + Lay::oINV);
   T* VcT = reinterpret_cast<T*>(smem + Lay::oVcT);
@@ -407,7 +429,8 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
   }
   if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
 
-  // ---- gate cumsum; qd, kd, ki row-major; S_in^T; INV
+  // ---- gate cumsum; qd, kd and the block-referenced q, k row-major; S_in^T; INV
+  bool strong_w = false;  // this wave's columns take block references
 #pragma unroll
   for (int ci = 0; ci < NCK; ++ci) {
     const int kt = wave + ci * NW;
@@ -417,22 +440,28 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
       tq[ci].get(qv, lane, len);
       tk[ci].get(kv, lane, len);
       col_prefix<RT>(G, lane);
+      float R[RT];
+      strong_w = choose_refs<RT>(G, R, lane) || strong_w;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        f32x4 q4, kd4, ki4;
+        f32x4 q4, ql4, kd4, ki4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float e = __expf(G[rt][j]);
           q4[j] = s.scale * qv[rt][j] * e;
+          ql4[j] = s.scale * qv[rt][j] * __expf(G[rt][j] - R[rt]);
           kd4[j] = kv[rt][j] * e;
-          ki4[j] = kv[rt][j] * __expf(-G[rt][j]);
+          ki4[j] = kv[rt][j] * __expf(R[rt] - G[rt][j]);
         }
+        if (grp == 0 && rt + 1 < RT) D[rt * K + 16 * kt + n] = __expf(R[rt + 1] - R[rt]);
         store_rows<T>(Qd, LDK, 16 * rt, 16 * kt, q4, lane, 1 << 30);
+        store_rows<T>(QL, LDK, 16 * rt, 16 * kt, ql4, lane, 1 << 30);
         store_rows<T>(Kd, LDK, 16 * rt, 16 * kt, kd4, lane, 1 << 30);
-        store_rows<T>(Ki, LDK, 16 * rt, 16 * kt, ki4, lane, 1 << 30);
+        store_rows<T>(KiL, LDK, 16 * rt, 16 * kt, ki4, lane, 1 << 30);
       }
     }
   }
+  if (lane == 0) wflag[wave] = strong_w;
 #pragma unroll
   for (int i = 0; i < NSV; ++i) {
     if constexpr (BLK) {
@@ -501,12 +530,12 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
                                        st4(VcT + col * LDC + 16 * mt + 4 * grp, vc4);
                                      }
                                    }, wave, lane);
-  block_gemm<T, RT, RT, 1, NW, K>(
-      Qd, LDK, 1 << 30, Ki, LDK, [](int mt, int nt0, int& kb, int& ke) { if (nt0 > mt) ke = 0; },
-      [&](int, int mt, int nt0, f32x4(&acc)[1]) {
+  tri_tiles<T, RT, NW, K>(
+      QL, LDK, KiL, LDK, D, K, any_flag<NW>(wflag),
+      [&](int mt, int nt0, f32x4 acc) {
         f32x4 m4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) m4[j] = (16 * nt0 + n <= 16 * mt + 4 * grp + j) ? acc[0][j] : 0.f;
+        for (int j = 0; j < 4; ++j) m4[j] = (16 * nt0 + n <= 16 * mt + 4 * grp + j) ? acc[j] : 0.f;
         store_rows<T>(Mqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
       }, wave, lane);
   __syncthreads();

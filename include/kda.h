@@ -59,11 +59,12 @@ typedef struct {
     int32_t HV;       /* value heads (multiple of H)                                          */
     int32_t K;        /* key dimension (rows of the state)                                    */
     int32_t V;        /* value dimension (columns of the state)                               */
-    int32_t C;        /* chunk size. The chunk kernels factor e^(G_i - G_j) as e^(G_i) e^(-G_j)
-                         with G the chunk-local cumsum of g, in fp32: every chunk's G must
-                         stay above about -85 (no guard; below it results are not finite).
-                         C = 16 keeps per-token gates down to -5 in range, C = 64 down to a
-                         chunk mean of about -1.3.                                            */
+    int32_t C;        /* chunk size. The chunk kernels take each gate factor e^(G_i - G_j)
+                         (G: chunk-local cumsum of g) relative to the first row of the
+                         16-row block holding i or j, in fp32 and bf16: the gates of the 15
+                         tokens after any block's first row must sum to more than about -85
+                         (per-token gates >= -5.6 always are; no guard, beyond it results are
+                         not finite). The sum over a whole chunk is not limited.             */
     int32_t N;        /* number of sequences: B when dense, len(cu_seqlens) - 1 when packed   */
     const int32_t* cu_seqlens_dev;   /* [N+1] device copy, or NULL when dense                 */
     const int32_t* cu_seqlens_host;  /* [N+1] host copy with the same values (sizes the grids

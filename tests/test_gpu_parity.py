@@ -222,6 +222,36 @@ def test_strong_decay_c16(oracle_mod):
         assert np.all(g_ce <= np.maximum(TOL["bf16"], 2 * m_ce + 1e-3)), key
 
 
+@pytest.mark.parametrize("channels", ["all", "upper_half", "one"])
+def test_strong_decay_c64(oracle_mod, channels):
+    """Per-token gates in [-5, -0.5] with C = 64: a chunk-local cumsum reaches -100 to -320,
+    where e^{-G} alone is beyond fp32 (and e^{G} below it). The kernels refer each 16-row
+    block to its first row wherever a wave's columns need it, so no factor they form exceeds
+    e^{85}; every output is finite and within the bf16 tolerance per tensor. The strong gates
+    cover every channel, the upper half of the channels (waves with and without block
+    references in one chunk) or a single channel. Per (chunk, head) the error is held to
+    three times the tolerance."""
+    w = small_workload("strong_decay_c64", B=2, T=150, H=2, HV=4, C=64, has_h0=True, has_dsf=True)
+    inp = kin.make_inputs(w, seed=23)
+    gen = torch.Generator().manual_seed(24)
+    strong = -(0.5 + 4.5 * torch.rand(inp["g"].shape, generator=gen))
+    if channels == "all":
+        inp["g"] = strong
+    elif channels == "upper_half":
+        inp["g"][..., 64:] = strong[..., 64:]
+    else:
+        inp["g"][..., 37] = strong[..., 37]
+    assert float(inp["g"].min()) >= -5.0
+    out = run_gpu(inp)
+    for key in GRADS + ["o", "final_state"]:
+        assert out.get(key) is not None and np.isfinite(out[key]).all(), key
+    ref = run_oracle(oracle_mod, inp)
+    errs, bad = compare(inp, out, ref)
+    _report(f"strong decay C=64 {channels}", errs)
+    assert not {k: v for k, v in bad.items() if "@chunk" not in k}, bad
+    assert all(v <= 3 * TOL["bf16"] for k, v in errs.items() if "@chunk" in k), errs
+
+
 @pytest.mark.parametrize("name", ["dense_ragged", "gva_ragged"])
 def test_error_matches_bf16_model(oracle_mod, name):
     """The kernels lose no more precision than a bf16 implementation should: each gradient's
