@@ -286,6 +286,9 @@ def summarize(res):
            "token_heads_per_s": th / (ms * 1e-3), "algorithmic_bytes": abytes, "algorithmic_flops": aflops,
            "t_roofline_ms": t_roof * 1e3, "call_frac": t_roof / (ms * 1e-3),
            "kernels_ms_cold": {k: statistics.median(v) for k, v in res["cold_kern"].items()}}
+    traffic = recorded_traffic(w.name)
+    out["traffic"] = traffic  # rocprofv3 HBM bytes per call, or None (see recorded_traffic)
+    out["traffic_over_algorithmic"] = None if traffic is None else traffic / abytes
     if "warm_calls" in res:
         out["ms_warm_median"] = statistics.median(res["warm_calls"])
         out["kernels_ms_warm"] = {k: statistics.median(v) for k, v in res["warm_kern"].items()}

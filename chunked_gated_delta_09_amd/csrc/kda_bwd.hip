@@ -424,9 +424,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     constexpr int NSV = (K * V / VEC + NTH - 1) / NTH;
     // with one column tile per wave, the row pieces of S_in this wave loads here (blocks
     // wave + i NW: rows 16 wave + n, columns 32 i + 8 grp) are the B fragments of its phase-3
-    // products, kept in registers instead of loading S_in a second time (not with grouped
-    // value heads, whose per-group accumulators leave no room for them)
-    constexpr bool SIN_REUSE = !GVA && BLK && NCT == 1 && KT == NW && NSV == V / M::KS;
+    // products, kept in registers instead of loading S_in a second time
+    constexpr bool SIN_REUSE = BLK && NCT == 1 && KT == NW && NSV == V / M::KS;
     vecT sv[NSV];
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
