@@ -98,8 +98,9 @@ kda_status validate(const kda_dims* d, Plan& p, bool launching) {
     p.NT = (int64_t)d->B * ((d->T + d->C - 1) / d->C);
   }
   if (p.NT > (int64_t)1 << 30) return fail(KDA_EINVAL, "too many chunks (%lld)", (long long)p.NT);
-  // the chunk kernels launch one workgroup per (chunk, head) on a one-dimensional grid
-  if (p.NT * d->HV > (int64_t)INT32_MAX)
+  // the chunk kernels launch one workgroup per (chunk, head) on a one-dimensional grid,
+  // rounded up to whole runs of 8 q/k groups
+  if (p.NT * d->HV + 8 * (int64_t)(d->HV / d->H) > (int64_t)INT32_MAX)
     return fail(KDA_EINVAL, "too many chunk-heads (%lld chunks x %d value heads)", (long long)p.NT, d->HV);
   return KDA_OK;
 }

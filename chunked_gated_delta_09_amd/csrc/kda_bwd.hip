@@ -85,8 +85,11 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
   T* QpT = reinterpret_cast<T*>(smem + Lay::oQpT);
   float* betas = reinterpret_cast<float*>(smem + Lay::oBeta);
 
-  // heads of one chunk are neighbouring workgroups: together they read whole token rows
-  const int c = blockIdx.x / s.nhv, h = s.hv0 + blockIdx.x % s.nhv;
+  // heads of one chunk are neighbouring workgroups (together they read whole token rows), a
+  // q/k group's on one XCD
+  const int task = group_task(blockIdx.x, s.HV / s.H, s.NT * s.nhv);
+  if (task < 0) return;
+  const int c = task / s.nhv, h = s.hv0 + task % s.nhv;
   const int hq = h / (s.HV / s.H);
   const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, grp = lane >> 4;
@@ -1064,7 +1067,7 @@ template <class T, int K, int V, int C>
 static hipError_t bwd_prep_t(const Shape& s, const void* q, const void* k, const float* g, const float* beta,
                              const void* inv, const void* dO, const BwdWs& ws, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C>), dim3(s.NT * s.nhv), dim3(64 * BwdPrepLds<T, K, V, C>::NW), 0, st, s,
+  hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C>), dim3(group_grid(s.NT * s.nhv, s.HV / s.H)), dim3(64 * BwdPrepLds<T, K, V, C>::NW), 0, st, s,
                      static_cast<const T*>(q), static_cast<const T*>(k), g, beta, static_cast<const T*>(inv),
                      static_cast<const T*>(dO), ws);
   return hipGetLastError();

@@ -679,6 +679,20 @@ __device__ __forceinline__ void tri_tiles(const T* A, int lda, const T* Bt, int 
   }
 }
 
+// Task of a per-(chunk, value head) workgroup, t = chunk-major index c * nhv + local head,
+// dealt so that the G value heads of one q/k group share an XCD (and its L2, which then
+// serves their common q and k rows once): workgroups go to the 8 XCDs round-robin by
+// linear id, so within each run of 8 G ids, id base + 8 e + gi holds member e of the run's
+// group gi. Launch group_grid(total, G) workgroups; ids past the last task get -1.
+__host__ __device__ inline int group_grid(int total, int G) {
+  return G == 1 ? total : (total + 8 * G - 1) / (8 * G) * (8 * G);
+}
+__device__ __forceinline__ int group_task(int b, int G, int total) {
+  const int run = 8 * G, base = (b / run) * run, rem = b % run;
+  const int t = base + (rem % 8) * G + rem / 8;
+  return t < total ? t : -1;
+}
+
 // Contraction-range helpers for triangular operands (K step = KS, tiles of 16 rows).
 template <class T>
 __device__ __forceinline__ int round_dn(int x) { return (x / Mma<T>::KS) * Mma<T>::KS; }

@@ -150,9 +150,12 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
   T* BVT = reinterpret_cast<T*>(smem + Lay::oBVT);
   float* betas = reinterpret_cast<float*>(smem + Lay::oBeta);
 
-  // heads of one chunk are neighbouring workgroups, chunks in reverse order: the first chunks,
-  // which the forward scan reads first, are the last ones written
-  const int c = s.NT - 1 - (int)(blockIdx.x / s.nhv), h = s.hv0 + blockIdx.x % s.nhv;
+  // heads of one chunk are neighbouring workgroups (a q/k group's on one XCD), chunks in
+  // reverse order: the first chunks, which the forward scan reads first, are the last ones
+  // written
+  const int task = group_task(blockIdx.x, s.HV / s.H, s.NT * s.nhv);
+  if (task < 0) return;
+  const int c = s.NT - 1 - task / s.nhv, h = s.hv0 + task % s.nhv;
   const int hq = h / (s.HV / s.H);
   const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, grp = lane >> 4;
@@ -351,9 +354,12 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
   T* UT = reinterpret_cast<T*>(smem + Lay::oUT);
   float* betas = reinterpret_cast<float*>(smem + Lay::oBeta);
 
-  // heads of one chunk are neighbouring workgroups, chunks in reverse order: the last chunks'
-  // states, the last ones the forward scan wrote, are read first
-  const int c = s.NT - 1 - (int)(blockIdx.x / s.nhv), h = s.hv0 + blockIdx.x % s.nhv;
+  // heads of one chunk are neighbouring workgroups (a q/k group's on one XCD), chunks in
+  // reverse order: the last chunks' states, the last ones the forward scan wrote, are read
+  // first
+  const int task = group_task(blockIdx.x, s.HV / s.H, s.NT * s.nhv);
+  if (task < 0) return;
+  const int c = s.NT - 1 - task / s.nhv, h = s.hv0 + task % s.nhv;
   const int hq = h / (s.HV / s.H);
   const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, grp = lane >> 4;
@@ -566,7 +572,7 @@ template <class T, int K, int V, int C>
 static hipError_t fwd_prep_t(const Shape& s, const void* k, const void* v, const float* g, const float* beta,
                              void* inv, const FwdWs& ws, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_prep_kernel<T, K, V, C>), dim3(s.NT * s.nhv), dim3(512), 0, st, s,
+  hipLaunchKernelGGL((fwd_prep_kernel<T, K, V, C>), dim3(group_grid(s.NT * s.nhv, s.HV / s.H)), dim3(512), 0, st, s,
                      static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<T*>(inv), ws);
   return hipGetLastError();
 }
@@ -582,7 +588,7 @@ template <class T, int K, int V, int C>
 static hipError_t fwd_out_t(const Shape& s, const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const void* states, const void* inv, void* o, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_out_kernel<T, K, V, C>), dim3(s.NT * s.nhv), dim3(512), 0, st, s,
+  hipLaunchKernelGGL((fwd_out_kernel<T, K, V, C>), dim3(group_grid(s.NT * s.nhv, s.HV / s.H)), dim3(512), 0, st, s,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), g, beta,
                      static_cast<const T*>(states), static_cast<const T*>(inv), static_cast<T*>(o));
   return hipGetLastError();

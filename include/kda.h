@@ -81,7 +81,8 @@ typedef struct {
 } kda_dims;
 
 /* Total number of chunks NT = sum_n ceil(len_n / C); -1 if dims are invalid. Valid dims have
- * NT <= 2^30 and NT * HV <= 2^31 - 1 (the kernels launch one workgroup per chunk and head). */
+ * NT <= 2^30 and NT * HV + 8 HV / H <= 2^31 - 1 (the kernels launch one workgroup per chunk and
+ * head, rounded up to whole runs of 8 q/k groups). */
 int64_t kda_num_chunks(const kda_dims* dims);
 
 /* Workspace bytes needed by kda_fwd_states / kda_chunk_bwd; 0 if dims are invalid. The
