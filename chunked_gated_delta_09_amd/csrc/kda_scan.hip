@@ -157,13 +157,12 @@ __global__ __launch_bounds__(64) void scan_kernel(Shape s, const T* __restrict__
 // bf16 path. The per-chunk operands P1, P2 (shared by every column slice of a (sequence,
 // head)) and e^gam are stored in fragment order (ScanFrag): each is a run of 1 KB wave
 // blocks. A workgroup holds NC column slices of one (sequence, head), one compute wave per
-// slice, plus two helper waves:
-//  - a copy wave streams the shared operands of chunk i+2 into a three-slot LDS ring
-//    (global_load_lds, 16 bytes per lane, no registers) while chunk i is computed, and
-//    waits for chunk i+1's copies to land before the barrier that opens step i+1;
-//  - a touch wave keeps the operands TOUCH_AHEAD chunks further on moving into L2 (one
-//    4-byte load per 128-byte line into a scratch LDS word, never waited for until exit).
-// All waves meet at one barrier per chunk step. The compute waves read the fragments from
+// slice, plus a copy wave that streams the shared operands of chunk i+2 into a three-slot
+// LDS ring (global_load_lds, 16 bytes per lane, no registers) while chunk i is computed, and
+// waits for chunk i+1's copies to land before the barrier that opens step i+1 (a further
+// wave that touched the lines of later chunks into L2 ahead of the copies cost more than it
+// gave: with ~32 workgroups per XCD its lines were evicted before use, doubling the fetches
+// of the grouped-head workloads). All waves meet at one barrier per chunk step. The compute waves read the fragments from
 // LDS (contiguous 16-byte reads per lane, issued well ahead of their MFMAs); their own
 // slice's seed tiles (W or Z) come through the ring too when a workgroup holds at most 4
 // slices, and otherwise from global memory one step ahead into a register double buffer.
@@ -210,7 +209,7 @@ struct ScanRing {
 };
 
 template <int K, int V, int C, bool FWD, int NC>
-__global__ __launch_bounds__(64 * (NC + 2)) void scan_bf16_kernel(Shape s, const bf16* __restrict__ P1,
+__global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const bf16* __restrict__ P1,
                                                                   const bf16* __restrict__ P2, const bf16* __restrict__ Zs,
                                                                   const bf16* __restrict__ Ws, const float* __restrict__ eg,
                                                                   const bf16* __restrict__ X0, bf16* __restrict__ Xout,
@@ -284,45 +283,6 @@ __global__ __launch_bounds__(64 * (NC + 2)) void scan_bf16_kernel(Shape s, const
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
   }
-  if (wave == NC + 1) {
-    // touch wave: lanes cover this workgroup's share of the lines of P1 and P2 (split
-    // between the NG workgroups of the head), the lines of its slices' seed tiles, and e^gam
-    constexpr int TOUCH_AHEAD = 5;
-    constexpr int SHARED_LINES = (F::P1_ELEMS + F::P2_ELEMS) * 2 / 128;
-    constexpr int SH_PER = (SHARED_LINES + NG - 1) / NG;
-    constexpr int SEED_LINES = (FWD ? C : K) * 16 * 2 / 128;
-    constexpr int NLINES = SH_PER + NC * SEED_LINES + (K * 4 + 127) / 128;
-    __shared__ int sink[64];
-    const int vg = r % NG;
-    auto touch = [&](int ii) {
-      const long ch = (long)chunk_of(ii) * s.HV + h;
-#pragma unroll
-      for (int l0 = 0; l0 < NLINES; l0 += 64) {
-        const int l = min(l0 + lane, NLINES - 1);
-        const void* a;
-        if (l < SH_PER) {
-          const int sl = min(vg * SH_PER + l, SHARED_LINES - 1);
-          a = sl < F::P1_ELEMS / 64 ? (const void*)(P1 + ch * F::P1_ELEMS + 64 * sl)
-                                    : (const void*)(P2 + ch * F::P2_ELEMS + 64 * (sl - F::P1_ELEMS / 64));
-        } else if (l < SH_PER + NC * SEED_LINES) {
-          const int q = l - SH_PER, vt = vt0 + q / SEED_LINES, ql = q % SEED_LINES;
-          a = FWD ? (const void*)(Zs + ch * C * V + F::seed(vt, 0, CT, 0) + 64 * ql)
-                  : (const void*)(Ws + ch * K * V + F::seed(vt, 0, KT, 0) + 64 * ql);
-        } else {
-          a = eg + ch * K + 32 * (l - SH_PER - NC * SEED_LINES);
-        }
-        copy4_to_lds(a, sink);
-      }
-    };
-    for (int d = 2; d < TOUCH_AHEAD && d < nc; ++d) touch(d);
-    for (int ii = 0; ii < nc; ++ii) {
-      __builtin_amdgcn_s_barrier();
-      if (ii + TOUCH_AHEAD < nc) touch(ii + TOUCH_AHEAD);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    return;
-  }
-
   // ---- compute wave: slice vt of this (sequence, head)
   const int vt = vt0 + wave;
   const int vcol = FWD ? 16 * vt + n : ScanCols::col(vt, n);
@@ -529,7 +489,7 @@ static hipError_t scan_t(const Shape& s, const void* P1, const void* P2, const v
     while (nc < V / 16 && slices / nc > 256) nc *= 2;
     const int grid = ((pairs + 7) / 8) * 8 * (V / 16 / nc);
     auto go = [&](auto kern, int ncw) {
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (ncw + 2)), 0, st, s, static_cast<const bf16*>(P1),
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (ncw + 1)), 0, st, s, static_cast<const bf16*>(P1),
                          static_cast<const bf16*>(P2), static_cast<const bf16*>(Zi), static_cast<const bf16*>(Wi), eg,
                          static_cast<const bf16*>(X0), static_cast<bf16*>(Xout), static_cast<bf16*>(Yout), Xfin);
     };
