@@ -35,6 +35,7 @@ CPU_SHARE = 16               # host threads of one GPU's share of the box
 
 # Kernels of one kda_chunk_bwd call, in launch order (the chunk table only for packed sequences).
 BWD_KERNELS = ["bwd_prep", "bwd_scan", "bwd_grad"]
+FWD_KERNELS = ["fwd_prep", "fwd_scan", "fwd_out"]  # kda_fwd_states with o, after the chunk table
 # Sources whose text fixes the backward kernels and their workspace layout.
 BWD_SOURCES = ["kda_api.cpp", "kda_bwd.hip", "kda_scan.hip", "kda_device.h", "kda_launch.h"]
 TRAFFIC_RECORD = os.path.join(HERE, "profiles", "kda_chunk_bwd_w1_hbm_counters.md")
@@ -266,6 +267,22 @@ def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True):
         torch.cuda.synchronize()
         res["fwd_calls"] = [hip.elapsed(fwd_ev[2 * i], fwd_ev[2 * i + 1]) for i in range(steps)]
         hip.destroy(fwd_ev)
+        # per-kernel times of the same calls, from the library's events (separate passes)
+        fnames = (["chunk_table"] if nk == 4 else []) + FWD_KERNELS
+        nf = len(fnames)
+        fk_ev = hip.events(2 * nf * steps)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            flush_buf.fill_(i & 0xFF)
+            kmeas.set_kernel_events(
+                ctypes.cast(ctypes.byref(fk_ev, 2 * nf * i * ctypes.sizeof(ctypes.c_void_p)),
+                            ctypes.POINTER(ctypes.c_void_p)), 2 * nf)
+            fwd_step()
+        kmeas.set_kernel_events(None, 0)
+        torch.cuda.synchronize()
+        res["fwd_kern"] = {name: [hip.elapsed(fk_ev[2 * nf * i + 2 * j], fk_ev[2 * nf * i + 2 * j + 1])
+                                  for i in range(steps)] for j, name in enumerate(fnames)}
+        hip.destroy(fk_ev)
     del keep, fw, d, ws
     torch.cuda.empty_cache()
     return res
@@ -298,7 +315,8 @@ def summarize(res):
         out["forward"] = {"entry": "kda_fwd_states with o (chunk prep, forward state scan, output)",
                           "ms_cold_median": fms, "token_heads_per_s": th / (fms * 1e-3),
                           "algorithmic_bytes": fb, "achieved_GBps": fb / (fms * 1e-3) / 1e9,
-                          "hbm_frac": fb / (fms * 1e-3) / PEAK_HBM_BYTES}
+                          "hbm_frac": fb / (fms * 1e-3) / PEAK_HBM_BYTES,
+                          "kernels_ms_cold": {k: statistics.median(v) for k, v in res.get("fwd_kern", {}).items()}}
     return out
 
 
