@@ -33,6 +33,7 @@ INV, the state gradient of each chunk) and the outputs dq, dk, dv are rounded to
 (round to nearest even); products, sums and the elementwise gate algebra stay in fp64 (the
 FlashKDA backward page keeps its workspace in bf16 and does its math in fp32). Its
 per-tensor error against the fp64 definition predicts the error a bf16 kernel can expect.
+``f32_operands=True`` is the same model with fp32 rounding, for the fp32 path.
 """
 from __future__ import annotations
 
@@ -64,13 +65,18 @@ def _bf16(a):
     return torch.from_numpy(np.asarray(a, dtype=np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
 
 
+def _f32(a):
+    """Round to the nearest fp32 value, returned as fp64."""
+    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
 def chunked_fwd_bwd(q, k, v, g, beta, cu_seqlens, scale, C, h0=None, dO=None, dS_final=None, backward=True,
-                    bf16_operands=False):
+                    bf16_operands=False, f32_operands=False):
     """Returns o, S_T and (if backward) dq, dk, dv, dg, dbeta, dh0, plus the per-chunk
     intermediates ``states`` (S_in, [NT, HV, K, V]), ``dstates`` (gradient w.r.t. each
     chunk's S_out, [NT, HV, K, V]) and ``inv`` ([NT, HV, C, C], identity on padded rows).
-    ``bf16_operands``: the bf16 error model described in the module docstring."""
-    r = _bf16 if bf16_operands else (lambda a: a)
+    ``bf16_operands``, ``f32_operands``: the error models described in the module docstring."""
+    r = _bf16 if bf16_operands else (_f32 if f32_operands else (lambda a: a))
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     h0, dO, dS_final = _f64(h0), _f64(dO), _f64(dS_final)
     T, H, K = q.shape

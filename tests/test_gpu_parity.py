@@ -252,6 +252,64 @@ def test_strong_decay_c64(oracle_mod, channels):
     assert all(v <= 3 * TOL["bf16"] for k, v in errs.items() if "@chunk" in k), errs
 
 
+def test_strong_decay_some_chunks_packed_gva(oracle_mod):
+    """Strong gates ([-5, -0.5]) in the tokens of a few chunks only, on packed ragged sequences
+    with grouped heads at C = 64: chunk-heads with and without block references side by side in
+    one launch, and a strong chunk next to a sequence boundary."""
+    inp = _small_inputs("gva3_varlen")
+    cu = [int(x) for x in inp["cu_seqlens"]]
+    gen = torch.Generator().manual_seed(31)
+    strong = -(0.5 + 4.5 * torch.rand(inp["g"].shape, generator=gen))
+    g = inp["g"].clone()
+    # the second chunk of every sequence, and the last 40 tokens of the first
+    for a, b in zip(cu[:-1], cu[1:]):
+        g[:, a + 64:min(a + 128, b)] = strong[:, a + 64:min(a + 128, b)]
+    g[:, max(cu[0], cu[1] - 40):cu[1]] = strong[:, max(cu[0], cu[1] - 40):cu[1]]
+    inp["g"] = g
+    out = run_gpu(inp)
+    for key in GRADS + ["o", "final_state"]:
+        assert np.isfinite(out[key]).all(), key
+    ref = run_oracle(oracle_mod, inp)
+    errs, bad = compare(inp, out, ref)
+    _report("strong decay some chunks, packed GVA", errs)
+    assert not {k: v for k, v in bad.items() if "@chunk" not in k}, bad
+    assert all(v <= 3 * TOL["bf16"] for k, v in errs.items() if "@chunk" in k), errs
+
+
+def test_strong_decay_fp32_c16(oracle_mod):
+    """fp32 path (K = V = C = 16) with per-token gates in [-5.5, -4.5]: chunk-local cumsums reach
+    -72 to -88, so some chunks take the block reference (one block per chunk) and some do not.
+    Every output is held to the fp32 tolerance, except dg, which under this decay is mostly the
+    cancellation of pair terms: it is held to three times (plus 1e-6) what the chunk form
+    predicts with fp32-rounded operands, per tensor and per (chunk, head)."""
+    w = small_workload("strong_fp32", B=2, T=70, H=1, HV=2, K=16, V=16, C=16, dtype="f32",
+                       has_h0=True, has_dsf=True)
+    inp = kin.make_inputs(w, seed=41)
+    gen = torch.Generator().manual_seed(42)
+    inp["g"] = -(4.5 + 1.0 * torch.rand(inp["g"].shape, generator=gen))
+    out = run_gpu(inp)
+    for key in GRADS + ["o", "final_state"]:
+        assert np.isfinite(out[key]).all(), key
+    ref = run_oracle(oracle_mod, inp)
+    errs, bad = compare(inp, out, ref)
+    _report("strong decay fp32 C=16", errs)
+    assert not {k: v for k, v in bad.items() if not k.startswith("dg")}, bad
+    from tests.kda_cases import chunk_errors, gpu_on_heads
+    B, T = inp["B"], inp["T"]
+    f = lambda t: t.float().numpy().astype(np.float64).reshape(B * T, *t.shape[2:])
+    model = chunked_fwd_bwd(f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["g"]), f(inp["beta"]).reshape(B * T, -1),
+                            kin.flat_cu(inp), inp["scale"], w.C, h0=inp["h0"].double().numpy(), dO=f(inp["dO"]),
+                            dS_final=inp["dS_final"].double().numpy(), f32_operands=True)
+    got = gpu_on_heads(inp, out)
+    m_t = rel_l2(model["dg"], ref["dg"])
+    g_ce = chunk_errors(got["dg"], ref["dg"], kin.flat_cu(inp), w.C)
+    m_ce = chunk_errors(model["dg"], ref["dg"], kin.flat_cu(inp), w.C)
+    print(f"[strong decay fp32 C=16] dg gpu {errs['dg']:.2e} model {m_t:.2e}; per chunk gpu {g_ce.max():.2e} "
+          f"model {m_ce.max():.2e}", flush=True)
+    assert errs["dg"] <= max(TOL["f32"], 3 * m_t + 1e-6)
+    assert np.all(g_ce <= np.maximum(TOL["f32"], 3 * m_ce + 1e-6))
+
+
 @pytest.mark.parametrize("name", ["dense_ragged", "gva_ragged"])
 def test_error_matches_bf16_model(oracle_mod, name):
     """The kernels lose no more precision than a bf16 implementation should: each gradient's

@@ -295,7 +295,8 @@ def test_thread_count_does_not_change_bits(oracle_mod):
 def test_bf16_error_model_within_budget(oracle_mod):
     """The chunked reference with every product operand and kept tensor rounded to bf16 (an
     error model, not a definition) stays inside the 2e-2 per-tensor budget on a bf16 case with
-    ragged chunks, and its rounding is live (errors well above fp64 noise)."""
+    ragged chunks, and its rounding is live (errors well above fp64 noise); likewise its fp32
+    variant inside 1e-5."""
     from chunked_gated_delta_09_amd import inputs as kin
     from oracle.chunked import chunked_fwd_bwd
     from tests.kda_cases import GRADS, rel_l2, run_oracle, small_workload
@@ -309,7 +310,11 @@ def test_bf16_error_model_within_budget(oracle_mod):
     kw = dict(h0=inp["h0"].double().numpy(), dO=f(inp["dO"]), dS_final=inp["dS_final"].double().numpy())
     exact = chunked_fwd_bwd(*args, **kw)
     model = chunked_fwd_bwd(*args, bf16_operands=True, **kw)
+    model32 = chunked_fwd_bwd(*args, f32_operands=True, **kw)
     for key in GRADS + ["o"]:
         assert rel_l2(exact[key], ref[key]) < 1e-10, key
         e = rel_l2(model[key], ref[key])
         assert 1e-4 < e < 2e-2, (key, e)
+        # the fp32 variant of the model: well inside the fp32 budget, still above fp64 noise
+        e32 = rel_l2(model32[key], ref[key])
+        assert 1e-10 < e32 < 1e-5, (key, e32)
