@@ -379,7 +379,16 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
         bx[p][i] = (bf16)X[2 * p][i];
         bx[p][4 + i] = (bf16)X[2 * p + 1][i];
       }
-    if constexpr (FWD) {
+    if constexpr (FWD && NC <= 2) {
+      // S_in row-major: each 16 x 16 tile moved to the row layout by an MFMA against the
+      // identity (lane: row 16t + n, columns 16vt + 4grp ..), one 8-byte store per tile. With
+      // 4 or more slices per workgroup 2-byte column stores measured faster (workload B=4,
+      // T=4096, HV=32: forward 795 vs 803 us) and with 8 the registers are not there.
+      bf16* xo = Xout + ch * K * V;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+        st4(xo + (16 * t + n) * V + 16 * vt + 4 * grp, to_rows_bf16(X[t][0], X[t][1], X[t][2], X[t][3], lane));
+    } else if constexpr (FWD) {
       bf16* xo = Xout + ch * K * V;
 #pragma unroll
       for (int t = 0; t < KT; ++t)
