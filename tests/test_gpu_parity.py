@@ -392,3 +392,38 @@ def test_random_geometries(oracle_mod, i):
     errs, bad = compare(inp, out, ref)
     _report(f"rand {i}", errs)
     assert not bad, bad
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_geometries_strong_gates(oracle_mod, i):
+    """Random bf16 geometries (as above, C = 16 or 64, dense or packed) with per-token gates in
+    [-5.5, -0.5] on a random set of channels over a random token range: chunk-heads, waves and
+    columns with and without block references mixed at random. Per tensor within 2e-2, per
+    (chunk, head) within three times that (dg under strong decay is mostly cancellation)."""
+    inp, logits = _random_case(100 + i)
+    while inp["workload"].dtype != "bf16":
+        i += 1000
+        inp, logits = _random_case(100 + i)
+    w = inp["workload"]
+    rng = np.random.default_rng(900 + i)
+    g = inp["g"].clone()
+    ntok = g.shape[1]
+    a = int(rng.integers(0, max(1, ntok)))
+    b = int(rng.integers(a, ntok + 1))
+    chans = torch.from_numpy(rng.random(w.K) < rng.uniform(0.05, 1.0))
+    strong = -(0.5 + 5.0 * torch.from_numpy(rng.random(tuple(g.shape)).astype(np.float32)))
+    sel = torch.zeros_like(g, dtype=torch.bool)
+    sel[:, a:b, :, :] = chans
+    g = torch.where(sel, strong, g)
+    inp["g"] = g
+    print(f"[rand strong {i}] C={w.C} H={w.H} HV={w.HV} cu={inp['cu_seqlens']} B={inp['B']} T={inp['T']} "
+          f"tokens {a}:{b} channels {int(chans.sum())}", flush=True)
+    out = run_gpu(inp, beta_logits=logits)
+    for key in GRADS + ["o", "final_state"]:
+        if out.get(key) is not None:
+            assert np.isfinite(out[key]).all(), key
+    ref = run_oracle(oracle_mod, inp, beta_logits=logits)
+    errs, bad = compare(inp, out, ref)
+    _report(f"rand strong {i}", errs)
+    assert not {k: v for k, v in bad.items() if "@chunk" not in k}, bad
+    assert all(v <= 3 * TOL["bf16"] for k, v in errs.items() if "@chunk" in k), errs
