@@ -297,7 +297,7 @@ KDA_EXPORT kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const v
   bw.yT = ws + L.yT;
   if (p.varlen) KDA_HIP(kda::launch_chunk_offsets(dims->cu_seqlens_dev, dims->N, p.C, reinterpret_cast<int32_t*>(ws + L.choff), hs));
   KDA_HIP(kda::launch_bwd_prep(p.dtype, p.C, s, q, k, g, beta, inv, dO, bw, hs));
-  KDA_HIP(kda::launch_scan_bwd(p.dtype, p.C, s, bw, dS_final, dh0, hs));
+  KDA_HIP(kda::launch_scan_bwd(p.dtype, p.C, s, bw, dO, dS_final, dh0, hs));
   KDA_HIP(kda::launch_bwd_grad(p.dtype, p.C, s, q, k, v, g, beta, states, inv, dO, bw, dq, dk, dv, dg, dbeta, hs));
   return KDA_OK;
 }

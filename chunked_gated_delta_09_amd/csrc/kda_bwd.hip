@@ -33,7 +33,8 @@ extern "C" __attribute__((visibility("default"))) int kda_phase_ts_read(void* ho
 #endif
 
 // LDS plan of the bwd prep kernel, small enough for two workgroups per CU. Later buffers
-// overlay earlier ones that a barrier has retired:
+// overlay earlier ones that a barrier has retired (with QPT the kernel ends at Q'^T, written
+// straight to global memory):
 //   QL, KiL (phases 0-2: scale q e^(G - R), k e^(R - G), block-referenced) -> dO^T (phase 3)
 //   beta kd^T (phases 0-1a)        -> Q'^T (phases 2-3)
 //   INV (phases 0-1a)              -> Mqk (phases 1b-2)
@@ -61,8 +62,10 @@ struct BwdPrepLds {
 };
 
 // One workgroup per (chunk, value head); two fit on a CU (LDS plan above, at most 128
-// VGPRs), so one's loads overlap the other's products.
-template <class T, int K, int V, int C>
+// VGPRs), so one's loads overlap the other's products. QPT: the scan forms W = Q'^T dO
+// itself, so this kernel writes Q'^T in the scan's K x C fragment order instead of W, and
+// reads no dO.
+template <class T, int K, int V, int C, bool QPT>
 __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
                                                         const float* __restrict__ gp, const float* __restrict__ bp,
                                                         const T* __restrict__ invp, const T* __restrict__ dOp,
@@ -119,10 +122,12 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
       col_load<T, RT>(kv[ci], kc, qs, 16 * kt + n, grp, len);
     }
   }
+  if constexpr (!QPT) {
 #pragma unroll
-  for (int cv = 0; cv < NCV; ++cv) {
-    const int vt = wave + cv * NW;
-    if (vt < VT) col_load<T, RT>(dov[cv], dOc, vs, 16 * vt + n, grp, len);
+    for (int cv = 0; cv < NCV; ++cv) {
+      const int vt = wave + cv * NW;
+      if (vt < VT) col_load<T, RT>(dov[cv], dOc, vs, 16 * vt + n, grp, len);
+    }
   }
   typedef T vecT __attribute__((ext_vector_type(16 / sizeof(T))));
   constexpr int VEC = 16 / (int)sizeof(T), NIV = (C * C / VEC + NTH - 1) / NTH;
@@ -231,9 +236,15 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
           const float eR = scl ? __expf(Rt[mt * K + col]) : 1.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) qp4[j] = to_f(QL[(16 * mt + 4 * grp + j) * LDK + col]) * eR - acc[jb][j];
-          st4(QpT + col * LDC + 16 * mt + 4 * grp, qp4);
+          if constexpr (QPT) {
+            static_assert(sizeof(T) == 2 && ScanFrag<K, V, C>::P2_ELEMS <= V * K, "Q'^T fits the W buffer");
+            st4(reinterpret_cast<T*>(ws.bcT) + ch * V * K + ScanFrag<K, V, C>::p2(col, 16 * mt + 4 * grp), qp4);
+          } else {
+            st4(QpT + col * LDC + 16 * mt + 4 * grp, qp4);
+          }
         }
       }, wave, lane);
+  if constexpr (QPT) return;
   __syncthreads();  // QL, KiL, Mqk, W^T retired
   // dO^T over QL and KiL
 #pragma unroll
@@ -1067,9 +1078,16 @@ template <class T, int K, int V, int C>
 static hipError_t bwd_prep_t(const Shape& s, const void* q, const void* k, const float* g, const float* beta,
                              const void* inv, const void* dO, const BwdWs& ws, hipStream_t st) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C>), dim3(group_grid(s.NT * s.nhv, s.HV / s.H)), dim3(64 * BwdPrepLds<T, K, V, C>::NW), 0, st, s,
-                     static_cast<const T*>(q), static_cast<const T*>(k), g, beta, static_cast<const T*>(inv),
-                     static_cast<const T*>(dO), ws);
+  const dim3 grid(group_grid(s.NT * s.nhv, s.HV / s.H)), block(64 * BwdPrepLds<T, K, V, C>::NW);
+  if constexpr (sizeof(T) == 2) {
+    if (scan_wq(1, s, V)) {
+      hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C, true>), grid, block, 0, st, s, static_cast<const T*>(q),
+                         static_cast<const T*>(k), g, beta, static_cast<const T*>(inv), static_cast<const T*>(dO), ws);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C, false>), grid, block, 0, st, s, static_cast<const T*>(q),
+                     static_cast<const T*>(k), g, beta, static_cast<const T*>(inv), static_cast<const T*>(dO), ws);
   return hipGetLastError();
 }
 

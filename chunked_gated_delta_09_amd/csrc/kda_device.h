@@ -303,6 +303,18 @@ __device__ __forceinline__ f32x4 to_rows_bf16(float x0, float x1, float x2, floa
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, id, zero4(), 0, 0, 0);
 }
 
+// The forward move for one bf16 tile held in the row layout (this lane: row lane%16, columns
+// 4(lane/16) .. +3, as raw bf16 bits): an MFMA against the identity returns it in the
+// column-owner layout (column lane%16, rows 4(lane/16) .. +3), exactly. Whole-wave only.
+__device__ __forceinline__ f32x4 rows_to_cols_bf16(const short __attribute__((ext_vector_type(4))) raw, int lane) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const int n = lane & 15, grp = lane >> 4;
+  s4 id;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) id[j] = (4 * grp + j == n) ? (short)0x3f80 : (short)0;
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(raw, id, zero4(), 0, 0, 0);
+}
+
 // Writes the 16 x 16 tile this wave holds in the column-owner layout (x[j]: row
 // r0 + 4(lane/16) + j, column c0 + lane%16) into a row-major array with row stride ld,
 // skipping rows >= rmax. bf16: transposed by to_rows_bf16, one 8-byte piece per lane

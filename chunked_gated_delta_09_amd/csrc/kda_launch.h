@@ -33,11 +33,26 @@ struct FwdWs {
 struct BwdWs {
   void* kr;    // [C][K]   k e^(gam-G)
   void* nwT;   // [K][C]   -w^T
-  void* bcT;   // [V][K]   (qd - Mqk w)^T dO, transposed
+  void* bcT;   // [V][K]   W = Q'^T dO, transposed (Q' = qd - Mqk w); or, where the scan forms W
+               //          itself (scan_wq), Q'^T [K][C] in the scan's fragment order
   float* eg;   // [K]      e^gam
   void* dS;    // [K][V]   gradient w.r.t. each chunk's S_out
   void* yT;    // [V][C]   (kr dS)^T
 };
+
+// Value slices (16 columns each) per workgroup of the bf16 scans: the fewest that keep the
+// grid within about one workgroup per CU.
+inline int scan_slices(const Shape& s, int V) {
+  const int slices = s.N * s.nhv * (V / 16);
+  int nc = 1;
+  while (nc < V / 16 && slices / nc > 256) nc *= 2;
+  return nc;
+}
+// The bf16 reverse scan forms W = Q'^T dO itself when a workgroup holds 4 or more slices (its
+// step is then bound by operand reads, and W's bytes exceed those of Q'^T and dO); with fewer
+// it reads W as precomputed seed tiles (its step is a dependency chain that extra products
+// would lengthen).
+inline bool scan_wq(int dtype, const Shape& s, int V) { return dtype != 0 && scan_slices(s, V) >= 4; }
 
 // dtype: 0 = fp32 (K = V = C = 16), 1 = bf16 (K = V = 128, C in {16, 64}).
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int C, int32_t* choff, hipStream_t st);
@@ -50,8 +65,8 @@ hipError_t launch_scan_fwd(int dtype, int C, const Shape& s, const FwdWs& ws, co
                            float* final_state, hipStream_t st);
 hipError_t launch_bwd_prep(int dtype, int C, const Shape& s, const void* q, const void* k, const float* g,
                            const float* beta, const void* inv, const void* dO, const BwdWs& ws, hipStream_t st);
-hipError_t launch_scan_bwd(int dtype, int C, const Shape& s, const BwdWs& ws, const void* dSf, float* dh0,
-                           hipStream_t st);
+hipError_t launch_scan_bwd(int dtype, int C, const Shape& s, const BwdWs& ws, const void* dO, const void* dSf,
+                           float* dh0, hipStream_t st);
 hipError_t launch_bwd_grad(int dtype, int C, const Shape& s, const void* q, const void* k, const void* v,
                            const float* g, const float* beta, const void* states, const void* inv, const void* dO,
                            const BwdWs& ws, void* dq, void* dk, void* dv, float* dg, float* dbeta, hipStream_t st);

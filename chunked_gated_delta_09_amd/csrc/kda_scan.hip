@@ -191,20 +191,28 @@ __device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory", "m0");
 }
 
-// Ring slot layout, in 1 KB blocks: P1 fragments, P2 fragments, e^gam, then (SEED_DMA) the
-// seed tiles of the NC slices.
+// Ring slot layout, in 1 KB blocks: P1 fragments, P2 fragments, e^gam, then either (WQ) the
+// Q'^T fragments (P2's layout) and the dO rows of the slices' 32-column groups (C rows x 64
+// bytes per group: the columns of slices 2m and 2m + 1 are the value columns 32m .. 32m + 31),
+// or (SEED_DMA) the seed tiles of the NC slices.
 template <int K, int V, int C, bool FWD, int NC>
 struct ScanRing {
   typedef ScanFrag<K, V, C> F;
+  // backward with 4 or more slices per workgroup (scan_wq): each slice forms its W = Q'^T dO
+  static constexpr bool WQ = !FWD && NC >= 4;
   static constexpr int NB1 = F::CT * F::KP, NB2 = F::KT * F::CQ;  // 1 KB blocks of P1, P2
-  static constexpr int OE = NB1 + NB2, OS = OE + 1;                 // e^gam block, first seed block
+  static constexpr int OE = NB1 + NB2, O3 = OE + 1;                 // e^gam block, first Q'^T block
+  static constexpr int NB3 = WQ ? NB2 : 0;
+  static constexpr int NPAIR = (NC + 1) / 2, DKB = C / 16;          // dO: groups, 1 KB blocks per group
+  static constexpr int OS = O3 + NB3;                               // first seed / dO block
   static constexpr int SROWS = FWD ? F::CT : F::KT;                 // 16-row seed tiles per slice
-  static constexpr bool SEED_DMA = NC <= 4 && SROWS % 2 == 0;       // seeds through the ring
+  static constexpr bool SEED_DMA = !WQ && NC <= 4 && SROWS % 2 == 0;  // seeds through the ring
   static constexpr int SKB = SROWS / 2;                             // 1 KB blocks per slice's seeds
-  static constexpr int NL = OS + (SEED_DMA ? NC * SKB : 0);         // copies per chunk
+  static constexpr int NL = OS + (SEED_DMA ? NC * SKB : 0) + (WQ ? NPAIR * DKB : 0);  // copies per chunk
   static constexpr int SLOT = NL * 1024;
-  static constexpr int R = 3;  // ring slots
-  static_assert(NL <= 63, "the copy wave's wait count must fit vmcnt");
+  static constexpr int R = 3 * SLOT <= 160 * 1024 ? 3 : 2;  // ring slots (the LDS of one CU)
+  static constexpr int LEAD = R - 1;                         // chunks copied ahead of the step
+  static_assert(LEAD == 1 || NL <= 63, "the copy wave's wait count must fit vmcnt");
   static_assert(K % 4 == 0 && K * 4 <= 1024, "e^gam fits one block");
 };
 
@@ -213,10 +221,12 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
                                                                   const bf16* __restrict__ P2, const bf16* __restrict__ Zs,
                                                                   const bf16* __restrict__ Ws, const float* __restrict__ eg,
                                                                   const bf16* __restrict__ X0, bf16* __restrict__ Xout,
-                                                                  bf16* __restrict__ Yout, float* __restrict__ Xfin) {
+                                                                  bf16* __restrict__ Yout, float* __restrict__ Xfin,
+                                                                  const bf16* __restrict__ dO) {
   typedef ScanFrag<K, V, C> F;
   typedef ScanRing<K, V, C, FWD, NC> RG;
   typedef Mma<bf16> M;
+  typedef short s4 __attribute__((ext_vector_type(4)));
   constexpr int KT = F::KT, CT = F::CT, KP = F::KP, CQ = F::CQ, VT = V / 16;
   static_assert(KT % 2 == 0, "the bf16 scan pairs row tiles of X");
   static_assert(VT % NC == 0, "a workgroup holds whole slices");
@@ -244,6 +254,12 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
   if (wave == NC) {
     // copy wave: chunk index clamped to the last one, so every step issues exactly NL
     // copies and the wait count below is exact
+    long sbos = (long)nseq * s.T;  // first token of the sequence, and its length
+    int slen = s.T;
+    if (s.cu != nullptr) {
+      sbos = s.cu[nseq];
+      slen = s.cu[nseq + 1] - s.cu[nseq];
+    }
     auto copy = [&](int ii) {
       const long ch = (long)chunk_of(min(ii, nc - 1)) * s.HV + h;
       unsigned char* slot = ring + (ii % RG::R) * RG::SLOT;
@@ -255,6 +271,23 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
       for (int b = 0; b < RG::NB2; ++b)
         copy16_to_lds(p2 + 512 * b, slot + 1024 * (RG::NB1 + b));
       copy16_to_lds(eg + ch * K + 4 * (lane % (K / 4)), slot + 1024 * RG::OE);
+      if constexpr (RG::WQ) {
+        const bf16* p3 = Ws + ch * K * V + 8 * lane;  // Q'^T in the W buffer
+#pragma unroll
+        for (int b = 0; b < RG::NB3; ++b) copy16_to_lds(p3 + 512 * b, slot + 1024 * (RG::O3 + b));
+        // dO rows of the chunk (rows past its end repeat its last row: Q' is zero there),
+        // lane: row 16 b + lane / 4, columns 8 (lane % 4) .. +7 of the group
+        const int lc = nc - 1 - min(ii, nc - 1);
+        const long bos = sbos + (long)lc * C;
+        const int len = min(C, slen - lc * C);
+        const bf16* d0 = dO + (bos * s.HV + h) * V + 32 * (vt0 >> 1) + 8 * (lane & 3);
+#pragma unroll
+        for (int pp = 0; pp < RG::NPAIR; ++pp)
+#pragma unroll
+          for (int b = 0; b < RG::DKB; ++b)
+            copy16_to_lds(d0 + (long)min(16 * b + (lane >> 2), len - 1) * s.HV * V + 32 * pp,
+                          slot + 1024 * (RG::OS + pp * RG::DKB + b));
+      }
       if constexpr (RG::SEED_DMA) {
         const bf16* sd = (FWD ? Zs + ch * C * V : Ws + ch * K * V) + 8 * lane;
 #pragma unroll
@@ -264,21 +297,21 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
             copy16_to_lds(sd + F::seed(vt0 + w, 0, RG::SROWS, 0) + 512 * b, slot + 1024 * (RG::OS + w * RG::SKB + b));
       }
     };
-    // Chunk j is copied into slot j % R during step j - 2, lands before the barrier that
+    // Chunk j is copied into slot j % R during step j - LEAD, lands before the barrier that
     // opens step j, and is read during that step.
     if (nc > 0) {
-      copy(0);
-      copy(1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RG::NL) : "memory");  // chunk 0 landed
+#pragma unroll
+      for (int j = 0; j < RG::LEAD; ++j) copy(j);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RG::NL * (RG::LEAD - 1)) : "memory");  // chunk 0 landed
     }
     for (int ii = 0; ii < nc; ++ii) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      // slot (ii + 2) % R was last read during step ii - 1
-      copy(ii + 2);
-      // chunk ii + 1 has landed (only the copies just issued may still be in flight)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RG::NL) : "memory");
+      // slot (ii + LEAD) % R was last read during step ii - 1
+      copy(ii + RG::LEAD);
+      // chunk ii + 1 has landed (only the copies of later chunks may still be in flight)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RG::NL * (RG::LEAD - 1)) : "memory");
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
@@ -290,7 +323,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
     bf16x4 t[FWD ? CT : KT];
   };
   auto load_seed = [&](int ii, Seed& o) {
-    if constexpr (RG::SEED_DMA) return;  // read from the ring at its step instead
+    if constexpr (RG::SEED_DMA || RG::WQ) return;  // read from the ring at its step instead
     const long ch = (long)chunk_of(min(ii, nc - 1)) * s.HV + h;
     if constexpr (FWD) {
 #pragma unroll
@@ -332,14 +365,20 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
     const unsigned char* slot = ring + (ii % RG::R) * RG::SLOT;
     const bf16x8* a1 = reinterpret_cast<const bf16x8*>(slot) + lane;
     const bf16x8* a2 = reinterpret_cast<const bf16x8*>(slot + 1024 * RG::NB1) + lane;
+    const bf16x8* a3 = reinterpret_cast<const bf16x8*>(slot + 1024 * RG::O3) + lane;
+    // WQ: this lane's row piece of dO tile m (row 16m + n, slice columns 4grp .. +3: bytes
+    // 16grp + 8(vt % 2) of the group's 64-byte row) at dslot + 1024 m
+    const unsigned char* dslot = slot + 1024 * (RG::OS + ((vt >> 1) - (vt0 >> 1)) * RG::DKB) + 64 * n + 16 * grp + 8 * (vt & 1);
     const float* eslot = reinterpret_cast<const float*>(slot + 1024 * RG::OE);
     const bf16x4* sslot = reinterpret_cast<const bf16x4*>(slot + 1024 * (RG::OS + wave * RG::SKB)) + lane;
 
     // With PIPE the ring is read in this program order -- forward: seed, P1 fragments,
-    // e^gam, P2 fragments; backward: P1 fragments, e^gam, seed, P2 fragments -- and the
-    // schedule at the end of the step issues each read well ahead of its use. Without PIPE
-    // the reads stay at their uses and the compiler schedules them.
-    bf16x8 f1[PIPE ? CT : 1][KP], f2[PIPE ? KT : 1][CQ];
+    // e^gam, P2 fragments; backward: P1 fragments, e^gam, seed or (WQ) dO pieces and Q'^T
+    // fragments, P2 fragments -- and the schedule at the end of the step issues each read well
+    // ahead of its use. Without PIPE the reads stay at their uses and the compiler schedules
+    // them.
+    bf16x8 f1[PIPE ? CT : 1][KP], f2[PIPE ? KT : 1][CQ], f3[PIPE && RG::WQ ? KT : 1][CQ];
+    s4 dr[PIPE && RG::WQ ? CT : 1];
     f32x4 ev[PIPE ? KT : 1];
     bf16x4 sd[RG::SEED_DMA ? RG::SROWS : 1];
     auto read_seed = [&]() {
@@ -357,6 +396,14 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
 #pragma unroll
       for (int t = 0; t < KT; ++t) ev[t] = *reinterpret_cast<const f32x4*>(eslot + 16 * t + 4 * grp);
       if constexpr (!FWD) read_seed();
+      if constexpr (RG::WQ) {
+#pragma unroll
+        for (int m = 0; m < CT; ++m) dr[m] = *reinterpret_cast<const s4*>(dslot + 1024 * m);
+#pragma unroll
+        for (int q = 0; q < CQ; ++q)
+#pragma unroll
+          for (int t = 0; t < KT; ++t) f3[t][q] = a3[(t * CQ + q) * 64];
+      }
 #pragma unroll
       for (int t = 0; t < KT; ++t)
 #pragma unroll
@@ -366,6 +413,12 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
     }
     auto F1 = [&](int m, int p) { if constexpr (PIPE) return f1[m][p]; else return a1[(m * KP + p) * 64]; };
     auto F2 = [&](int t, int q) { if constexpr (PIPE) return f2[t][q]; else return a2[(t * CQ + q) * 64]; };
+    auto F3 = [&](int t, int q) {
+      if constexpr (PIPE && RG::WQ) return f3[t][q]; else return a3[(t * CQ + q) * 64];
+    };
+    auto DR = [&](int m) {
+      if constexpr (PIPE && RG::WQ) return dr[m]; else return *reinterpret_cast<const s4*>(dslot + 1024 * m);
+    };
     auto EV = [&](int t) {
       if constexpr (PIPE) return ev[t]; else return *reinterpret_cast<const f32x4*>(eslot + 16 * t + 4 * grp);
     };
@@ -427,9 +480,36 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       X[t] = EV(t) * X[t];
-      if constexpr (!FWD) {
+      if constexpr (!FWD && !RG::WQ) {
         const bf16x4 w = SD(t);
         X[t] += f32x4{(float)w[0], (float)w[1], (float)w[2], (float)w[3]};
+      }
+    }
+    if constexpr (RG::WQ) {
+      // W = Q'^T dO: the dO tiles, moved to the column-owner layout by MFMAs against the
+      // identity, are B fragments (rows 32q + 4grp + i in slots 0-3, 32q + 16 + 4grp + i in
+      // slots 4-7: the order of P2's fragments)
+#pragma unroll
+      for (int q = 0; q < CQ; ++q) {
+        const bool pair2 = 2 * q + 1 < CT;
+        const f32x4 lo = rows_to_cols_bf16(DR(2 * q), lane);
+        f32x4 hi = zero4();
+        if (pair2) hi = rows_to_cols_bf16(DR(pair2 ? 2 * q + 1 : 0), lane);
+        bf16x8 b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b[i] = (bf16)lo[i];
+          b[4 + i] = (bf16)hi[i];
+        }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          bf16x8 a = F3(t, q);
+          if (!pair2) {
+#pragma unroll
+            for (int i = 4; i < 8; ++i) a[i] = (bf16)0.0f;
+          }
+          X[t] = M::mma(a, b, X[t]);
+        }
       }
     }
 #pragma unroll
@@ -454,7 +534,8 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
     if constexpr (PIPE) {
       // the first UP ring reads (at least everything the first product needs), then one
       // further read after each MFMA: every read is issued at least 8 MFMAs before its use
-      constexpr int NR = CT * KP + KT + KT * CQ + (RG::SEED_DMA ? RG::SROWS : 0), NMMA = CT * KP + KT * CQ;
+      constexpr int NR = CT * KP + KT + KT * CQ + (RG::SEED_DMA ? RG::SROWS : 0) + (RG::WQ ? CT + RG::NB3 : 0);
+      constexpr int NMMA = CT * KP + KT * CQ + (RG::WQ ? CT + KT * CQ : 0);
       constexpr int PRE = CT * KP + (FWD && RG::SEED_DMA ? RG::SROWS : 0);
       constexpr int UP = PRE > NR - NMMA + 8 ? PRE : NR - NMMA + 8;
       static_assert(UP <= NR && NR - UP <= NMMA, "the interleave covers every ring read");
@@ -488,19 +569,20 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
 
 template <class T, int K, int V, int C, bool FWD>
 static hipError_t scan_t(const Shape& s, const void* P1, const void* P2, const void* Zi, const void* Wi,
-                         const float* eg, const void* X0, void* Xout, void* Yout, float* Xfin, hipStream_t st) {
+                         const float* eg, const void* X0, void* Xout, void* Yout, float* Xfin, const void* dO,
+                         hipStream_t st) {
   if (s.N == 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    // Slices per workgroup: the fewest that keep the grid within about one workgroup per CU
-    // (the ring takes ~100 KB of LDS); more slices share one pull of the operands.
-    const int pairs = s.N * s.nhv, slices = pairs * (V / 16);
-    int nc = 1;
-    while (nc < V / 16 && slices / nc > 256) nc *= 2;
+    // Slices per workgroup (scan_slices): the fewest that keep the grid within about one
+    // workgroup per CU (the ring takes ~100-150 KB of LDS); more slices share one pull of the
+    // operands.
+    const int pairs = s.N * s.nhv, nc = scan_slices(s, V);
     const int grid = ((pairs + 7) / 8) * 8 * (V / 16 / nc);
     auto go = [&](auto kern, int ncw) {
       hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (ncw + 1)), 0, st, s, static_cast<const bf16*>(P1),
                          static_cast<const bf16*>(P2), static_cast<const bf16*>(Zi), static_cast<const bf16*>(Wi), eg,
-                         static_cast<const bf16*>(X0), static_cast<bf16*>(Xout), static_cast<bf16*>(Yout), Xfin);
+                         static_cast<const bf16*>(X0), static_cast<bf16*>(Xout), static_cast<bf16*>(Yout), Xfin,
+                         static_cast<const bf16*>(dO));
     };
     if (nc == 1) go(scan_bf16_kernel<K, V, C, FWD, 1>, 1);
     else if (nc == 2) go(scan_bf16_kernel<K, V, C, FWD, 2>, 2);
@@ -554,22 +636,24 @@ hipError_t launch_scan_fwd(int dtype, int C, const Shape& s, const FwdWs& ws, co
                            float* final_state, hipStream_t st) {
   if (dtype == 0)
     return scan_t<float, 16, 16, 16, true>(s, ws.negw, ws.krT, ws.uT, nullptr, ws.eg, h0, states, nullptr,
-                                           final_state, st);
+                                           final_state, nullptr, st);
   if (C == 64)
     return scan_t<bf16, 128, 128, 64, true>(s, ws.negw, ws.krT, ws.uT, nullptr, ws.eg, h0, states, nullptr,
-                                            final_state, st);
+                                            final_state, nullptr, st);
   return scan_t<bf16, 128, 128, 16, true>(s, ws.negw, ws.krT, ws.uT, nullptr, ws.eg, h0, states, nullptr,
-                                          final_state, st);
+                                          final_state, nullptr, st);
 }
 
-hipError_t launch_scan_bwd(int dtype, int C, const Shape& s, const BwdWs& ws, const void* dSf, float* dh0,
-                           hipStream_t st) {
+hipError_t launch_scan_bwd(int dtype, int C, const Shape& s, const BwdWs& ws, const void* dO, const void* dSf,
+                           float* dh0, hipStream_t st) {
   if (dtype == 0)
-    return scan_t<float, 16, 16, 16, false>(s, ws.kr, ws.nwT, nullptr, ws.bcT, ws.eg, dSf, ws.dS, ws.yT, dh0, st);
+    return scan_t<float, 16, 16, 16, false>(s, ws.kr, ws.nwT, nullptr, ws.bcT, ws.eg, dSf, ws.dS, ws.yT, dh0, dO,
+                                            st);
   if (C == 64)
-    return scan_t<bf16, 128, 128, 64, false>(s, ws.kr, ws.nwT, nullptr, ws.bcT, ws.eg, dSf, ws.dS, ws.yT, dh0,
+    return scan_t<bf16, 128, 128, 64, false>(s, ws.kr, ws.nwT, nullptr, ws.bcT, ws.eg, dSf, ws.dS, ws.yT, dh0, dO,
                                              st);
-  return scan_t<bf16, 128, 128, 16, false>(s, ws.kr, ws.nwT, nullptr, ws.bcT, ws.eg, dSf, ws.dS, ws.yT, dh0, st);
+  return scan_t<bf16, 128, 128, 16, false>(s, ws.kr, ws.nwT, nullptr, ws.bcT, ws.eg, dSf, ws.dS, ws.yT, dh0, dO,
+                                           st);
 }
 
 }  // namespace kda

@@ -40,6 +40,11 @@ SMALL = {
     "gva3_varlen": small_workload("gva3_varlen", H=2, HV=6, varlen=3, total=300, len_lo=20, len_hi=200,
                                   has_h0=True, has_dsf=True),
     "gva8": small_workload("gva8", B=1, T=96, H=1, HV=8, has_h0=False, has_dsf=True),
+    # enough (sequence, head) pairs that the reverse scan holds 4 (many_heads) or 8 (many_seqs)
+    # value slices per workgroup and forms W = Q'^T dO itself
+    "many_heads": small_workload("many_heads", B=1, T=200, H=72, HV=72, has_h0=True, has_dsf=True),
+    "many_seqs": small_workload("many_seqs", H=4, HV=8, varlen=40, total=3000, len_lo=0, len_hi=150,
+                                has_h0=True, has_dsf=True),
 }
 
 
@@ -53,6 +58,14 @@ def _small_inputs(name):
         for ln in lens:
             cu.append(cu[-1] + ln)
         inp["cu_seqlens"] = cu
+    if name == "many_seqs":
+        # an empty sequence, a single token and exact one- and two-chunk sequences among them
+        cu = inp["cu_seqlens"]
+        lens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+        lens[3], lens[7], lens[11], lens[12] = 0, 1, 64, 128
+        lens[-1] = cu[-1] - sum(lens[:-1])
+        assert lens[-1] >= 1
+        inp["cu_seqlens"] = [0] + [int(x) for x in np.cumsum(lens)]
     return inp
 
 
@@ -81,7 +94,7 @@ def test_stage_parity_states_and_inverse(oracle_mod):
     assert e_states < 1e-2 and e_inv < 1e-2
 
 
-@pytest.mark.parametrize("name", ["varlen_edges", "gva3_varlen", "c16"])
+@pytest.mark.parametrize("name", ["varlen_edges", "gva3_varlen", "c16", "many_heads", "many_seqs"])
 def test_stage_parity_state_gradients(name):
     """Per-chunk state gradients of the reverse scan (the dS_out each chunk's products consume;
     FlashKDA backward page, step 2) against the fp64 chunked reference's, on packed ragged
