@@ -464,6 +464,33 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         iv[i] = *reinterpret_cast<const vecT*>(invc + min(tid + i * NTH, C * C / VEC - 1) * VEC);
       }
     }
+    // v at the places of the C x V accumulator tiles this wave owns in the block walk of
+    // kd S_in and INV^T dU (same walk: RT x VT tiles in blocks of 1 x BN1)
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 vraw[NIT1][BN1];
+    ColTile<T, 1> tv[NIT1][BN1];
+#pragma unroll
+    for (int it = 0; it < NIT1; ++it) {
+      const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
+      const int mt = blk / (VT / BN1), nt0 = (blk % (VT / BN1)) * BN1;
+#pragma unroll
+      for (int jb = 0; jb < BN1; ++jb) tv[it][jb].load(vc, vs, 16 * (nt0 + jb), lane, len, 16 * mt);
+    }
+
+    // ---- phase 1 compute: column tiles of g, q, k and v into the column-owner layout; gate
+    // cumsum, block references R, block-referenced q and keys and decayed keys (row-major),
+    // S_in^T
+    if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
+#pragma unroll
+    for (int ci = 0; ci < NCT; ++ci) {
+      if (wave + ci * NW < KT) {
+        tg[ci].get(Gr[ci], lane, len);
+        tq[ci].get(qv[ci], lane, len);
+        tk[ci].get(kv[ci], lane, len);
+      }
+    }
+    // dO and (kr dS)^T are first used in phase 2: issued once the first tiles have arrived,
+    // so that the opening burst of every CU is smaller and these land during phase 1
     vecT dov[NDV];
 #pragma unroll
     for (int i = 0; i < NDV; ++i) {
@@ -478,18 +505,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       dov[i] = *reinterpret_cast<const vecT*>(dOc + min(row, len - 1) * vs + c);
       if (row >= len) dov[i] = vecT{};
     }
-    // v at the places of the C x V accumulator tiles this wave owns in the block walk of
-    // kd S_in and INV^T dU (same walk: RT x VT tiles in blocks of 1 x BN1)
-    typedef T t4 __attribute__((ext_vector_type(4)));
-    t4 vraw[NIT1][BN1];
-    ColTile<T, 1> tv[NIT1][BN1];
-#pragma unroll
-    for (int it = 0; it < NIT1; ++it) {
-      const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
-      const int mt = blk / (VT / BN1), nt0 = (blk % (VT / BN1)) * BN1;
-#pragma unroll
-      for (int jb = 0; jb < BN1; ++jb) tv[it][jb].load(vc, vs, 16 * (nt0 + jb), lane, len, 16 * mt);
-    }
     // (kr dS)^T at the places of the dU tiles this wave owns (same block walk), for the dU
     // epilogue
     t4 yraw[NIT1][BN1];
@@ -500,19 +515,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 #pragma unroll
       for (int jb = 0; jb < BN1; ++jb)
         yraw[it][jb] = *reinterpret_cast<const t4*>(yT + (16 * (nt0 + jb) + n) * C + 16 * mt + 4 * grp);
-    }
-
-    // ---- phase 1 compute: column tiles of g, q, k and v into the column-owner layout; gate
-    // cumsum, block references R, block-referenced q and keys and decayed keys (row-major),
-    // S_in^T
-    if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
-#pragma unroll
-    for (int ci = 0; ci < NCT; ++ci) {
-      if (wave + ci * NW < KT) {
-        tg[ci].get(Gr[ci], lane, len);
-        tq[ci].get(qv[ci], lane, len);
-        tk[ci].get(kv[ci], lane, len);
-      }
     }
 #pragma unroll
     for (int it = 0; it < NIT1; ++it) {
