@@ -464,18 +464,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         iv[i] = *reinterpret_cast<const vecT*>(invc + min(tid + i * NTH, C * C / VEC - 1) * VEC);
       }
     }
-    // v at the places of the C x V accumulator tiles this wave owns in the block walk of
-    // kd S_in and INV^T dU (same walk: RT x VT tiles in blocks of 1 x BN1)
-    typedef T t4 __attribute__((ext_vector_type(4)));
-    t4 vraw[NIT1][BN1];
-    ColTile<T, 1> tv[NIT1][BN1];
-#pragma unroll
-    for (int it = 0; it < NIT1; ++it) {
-      const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
-      const int mt = blk / (VT / BN1), nt0 = (blk % (VT / BN1)) * BN1;
-#pragma unroll
-      for (int jb = 0; jb < BN1; ++jb) tv[it][jb].load(vc, vs, 16 * (nt0 + jb), lane, len, 16 * mt);
-    }
 
     // ---- phase 1 compute: column tiles of g, q, k and v into the column-owner layout; gate
     // cumsum, block references R, block-referenced q and keys and decayed keys (row-major),
@@ -489,8 +477,21 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         tk[ci].get(kv[ci], lane, len);
       }
     }
-    // dO and (kr dS)^T are first used in phase 2: issued once the first tiles have arrived,
-    // so that the opening burst of every CU is smaller and these land during phase 1
+    // v, dO and (kr dS)^T are first used after the first barrier: issued once the first tiles
+    // have arrived, so that the opening burst of every CU is smaller and these land during
+    // phase 1
+    // v at the places of the C x V accumulator tiles this wave owns in the block walk of
+    // kd S_in and INV^T dU (same walk: RT x VT tiles in blocks of 1 x BN1)
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 vraw[NIT1][BN1];
+    ColTile<T, 1> tv[NIT1][BN1];
+#pragma unroll
+    for (int it = 0; it < NIT1; ++it) {
+      const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
+      const int mt = blk / (VT / BN1), nt0 = (blk % (VT / BN1)) * BN1;
+#pragma unroll
+      for (int jb = 0; jb < BN1; ++jb) tv[it][jb].load(vc, vs, 16 * (nt0 + jb), lane, len, 16 * mt);
+    }
     vecT dov[NDV];
 #pragma unroll
     for (int i = 0; i < NDV; ++i) {
@@ -515,18 +516,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
 #pragma unroll
       for (int jb = 0; jb < BN1; ++jb)
         yraw[it][jb] = *reinterpret_cast<const t4*>(yT + (16 * (nt0 + jb) + n) * C + 16 * mt + 4 * grp);
-    }
-#pragma unroll
-    for (int it = 0; it < NIT1; ++it) {
-      const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
-      const int mt = blk / (VT / BN1);
-#pragma unroll
-      for (int jb = 0; jb < BN1; ++jb) {
-        float x[1][4];
-        tv[it][jb].get(x, lane, len, 16 * mt);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vraw[it][jb][j] = from_f<T>(x[0][j]);
-      }
     }
     float gam[NCT];
     bool strong_c[NCT];  // column tile ci takes block references
@@ -632,6 +621,18 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
           for (int j = 0; j < 4; ++j) m4[j] = (16 * nt0 + n <= 16 * mt + 4 * grp + j) ? acc[j] : 0.f;
           st4(MqkT + (16 * nt0 + n) * LDC + 16 * mt + 4 * grp, m4);
         }, wave, lane);
+#pragma unroll
+    for (int it = 0; it < NIT1; ++it) {
+      const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
+      const int mt = blk / (VT / BN1);
+#pragma unroll
+      for (int jb = 0; jb < BN1; ++jb) {
+        float x[1][4];
+        tv[it][jb].get(x, lane, len, 16 * mt);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vraw[it][jb][j] = from_f<T>(x[0][j]);
+      }
+    }
     // ---- kd S_in -> vcorr^T = (beta (v - kd S_in))^T
     block_gemm<T, RT, VT, BN1, NW, K>(Kd, LDK, 1 << 30, SinT, LDK, FullRange(),
                                       [&](int it, int mt, int nt0, f32x4(&acc)[BN1]) {
