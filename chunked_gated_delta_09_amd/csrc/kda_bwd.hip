@@ -112,7 +112,7 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
   KDA_TS(0, 0);
   // ---- every global load of the chunk, issued before any use
   const float beta_raw = beta_of(bc[min(tid % C, len - 1) * s.HV], s.beta_logits);
-  float G[NCK][RT][4], qv[NCK][RT][4], kv[NCK][RT][4], dov[NCV][RT][4];
+  float G[NCK][RT][4], qv[NCK][RT][4], kv[NCK][RT][4];
 #pragma unroll
   for (int ci = 0; ci < NCK; ++ci) {
     const int kt = wave + ci * NW;
@@ -120,13 +120,6 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
       col_load<float, RT>(G[ci], gc, gs, 16 * kt + n, grp, len);
       col_load<T, RT>(qv[ci], qc, qs, 16 * kt + n, grp, len);
       col_load<T, RT>(kv[ci], kc, qs, 16 * kt + n, grp, len);
-    }
-  }
-  if constexpr (!QPT) {
-#pragma unroll
-    for (int cv = 0; cv < NCV; ++cv) {
-      const int vt = wave + cv * NW;
-      if (vt < VT) col_load<T, RT>(dov[cv], dOc, vs, 16 * vt + n, grp, len);
     }
   }
   typedef T vecT __attribute__((ext_vector_type(16 / sizeof(T))));
@@ -178,6 +171,19 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
     }
   }
   if (lane == 0) wflag[wave] = strong_w;
+  // dO (first used by W at the end): issued once g, q and k have arrived, so that the
+  // opening burst of the two workgroups of a CU is smaller and dO lands during the products
+  T dor[NCV][RT][4];
+  if constexpr (!QPT) {
+#pragma unroll
+    for (int cv = 0; cv < NCV; ++cv) {
+      const int vt = min(wave + cv * NW, VT - 1);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dor[cv][rt][j] = dOc[min(16 * rt + 4 * grp + j, len - 1) * vs + 16 * vt + n];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NIV; ++i) {
     const int pid = tid + i * NTH;
@@ -252,9 +258,12 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
     const int vt = wave + cv * NW;
     if (vt < VT) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        st4(DoT + (16 * vt + n) * LDC + 16 * rt + 4 * grp,
-            f32x4{dov[cv][rt][0], dov[cv][rt][1], dov[cv][rt][2], dov[cv][rt][3]});
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 d4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d4[j] = 16 * rt + 4 * grp + j < len ? to_f(dor[cv][rt][j]) : 0.f;
+        st4(DoT + (16 * vt + n) * LDC + 16 * rt + 4 * grp, d4);
+      }
     }
   }
   __syncthreads();
