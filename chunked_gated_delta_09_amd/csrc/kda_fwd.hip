@@ -423,16 +423,6 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
       iv[i] = *reinterpret_cast<const vecT*>(invc + min(tid + i * NTH, C * C / VEC - 1) * VEC);
     }
   }
-  // v at the places of the C x V accumulator tiles this wave owns in the block walk of the
-  // products below (RT x VT tiles in blocks of 1 x BN)
-  ColTile<T, 1> tv[NIT1][BN];
-#pragma unroll
-  for (int it = 0; it < NIT1; ++it) {
-    const int blk = min(wave + it * NW, RT * (VT / BN) - 1);
-    const int mt = blk / (VT / BN), nt0 = (blk % (VT / BN)) * BN;
-#pragma unroll
-    for (int jb = 0; jb < BN; ++jb) tv[it][jb].load(vc, vs, 16 * (nt0 + jb), lane, len, 16 * mt);
-  }
   if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
 
   // ---- gate cumsum; qd, kd and the block-referenced q, k row-major; S_in^T; INV
@@ -468,6 +458,18 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
     }
   }
   if (lane == 0) wflag[wave] = strong_w;
+  // v at the places of the C x V accumulator tiles this wave owns in the block walk of the
+  // products below (RT x VT tiles in blocks of 1 x BN), first used after the barrier below:
+  // issued once g, q and k have arrived, so that the opening burst of every CU is smaller and
+  // v lands during the stores below
+  ColTile<T, 1> tv[NIT1][BN];
+#pragma unroll
+  for (int it = 0; it < NIT1; ++it) {
+    const int blk = min(wave + it * NW, RT * (VT / BN) - 1);
+    const int mt = blk / (VT / BN), nt0 = (blk % (VT / BN)) * BN;
+#pragma unroll
+    for (int jb = 0; jb < BN; ++jb) tv[it][jb].load(vc, vs, 16 * (nt0 + jb), lane, len, 16 * mt);
+  }
 #pragma unroll
   for (int i = 0; i < NSV; ++i) {
     if constexpr (BLK) {
@@ -508,6 +510,7 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
       }
     }
   }
+  __syncthreads();
   t4 vraw[NIT1][BN];
 #pragma unroll
   for (int it = 0; it < NIT1; ++it) {
@@ -521,7 +524,6 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
       for (int j = 0; j < 4; ++j) vraw[it][jb][j] = from_f<T>(x[0][j]);
     }
   }
-  __syncthreads();
 
   // ---- vcorr = diag(beta)(v - kd S_in), stored transposed; Mqk = tril(qd ki^T), row-major
   block_gemm<T, RT, VT, BN, NW, K>(Kd, LDK, 1 << 30, SinT, LDK, FullRange(),
