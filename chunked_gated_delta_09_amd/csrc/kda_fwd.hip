@@ -169,8 +169,8 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
   const T* __restrict__ vc = vp + (geo.bos * s.HV + h) * V;
   const float* __restrict__ bc = bp + geo.bos * s.HV + h;
 
-  // ---- every global load, issued before any use (row pieces, moved to the column-owner
-  // layout by the tiles' MFMA transposes)
+  // ---- g and k loads, issued before any use (row pieces, moved to the column-owner layout by
+  // the tiles' MFMA transposes); v follows once they have arrived
   const float beta_raw = beta_of(bc[min(tid % C, len - 1) * s.HV], s.beta_logits);
   ColTile<float, RT> tg[NCK];
   ColTile<T, RT> tk[NCK], tv[NCV];
@@ -180,8 +180,6 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
     tg[ci].load(gc, gs, 16 * kt, lane, len);
     tk[ci].load(kc, qs, 16 * kt, lane, len);
   }
-#pragma unroll
-  for (int cv = 0; cv < NCV; ++cv) tv[cv].load(vc, vs, 16 * min(wave + cv * NW, VT - 1), lane, len);
   if (tid < C) betas[tid] = tid < len ? beta_raw : 0.f;
   __syncthreads();
 
@@ -226,15 +224,10 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
     }
   }
   if (lane == 0) wflag[wave] = strong_w;
-  float bv[NCV][RT][4];  // diag(beta) v in the column-owner layout, stored once L is retired
+  // v (first used once INV is known): issued once g and k have arrived, so that the opening
+  // burst of the two workgroups of a CU is smaller and v lands during L and the inverse
 #pragma unroll
-  for (int cv = 0; cv < NCV; ++cv) {
-    tv[cv].get(bv[cv], lane, len);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[cv][rt][j] *= betas[16 * rt + 4 * grp + j];
-  }
+  for (int cv = 0; cv < NCV; ++cv) tv[cv].load(vc, vs, 16 * min(wave + cv * NW, VT - 1), lane, len);
   __syncthreads();
 
   // ---- L = strict_tril(diag(beta) kd ki^T), fp32, from the block-referenced keys
@@ -253,6 +246,15 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
   unit_lower_inverse<C, NW>(Lf, Xf, LDL, wave, lane);
 
   // ---- INV to global memory and as the MFMA operand; diag(beta) v^T over L
+  float bv[NCV][RT][4];  // diag(beta) v in the column-owner layout
+#pragma unroll
+  for (int cv = 0; cv < NCV; ++cv) {
+    tv[cv].get(bv[cv], lane, len);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[cv][rt][j] *= betas[16 * rt + 4 * grp + j];
+  }
   T* __restrict__ inv = invp + ch * C * C;
   for (int i = tid; i < C * C / 4; i += 64 * NW) {
     const int row = (4 * i) / C, col = (4 * i) % C;
@@ -322,9 +324,10 @@ struct FwdOutLds {
 };
 
 // o = qd S_in + tril(qd ki^T) U with U = INV diag(beta)(v - kd S_in); one workgroup per
-// (chunk, value head), 512 threads. Every global load is issued before any use: g, q, k and
-// v as row pieces moved to the column-owner layout by MFMA transposes, S_in and INV as
-// 16-byte pieces (bf16: 16 x 32 blocks, written transposed into LDS by MFMA transposes).
+// (chunk, value head), 512 threads. g, q, k, S_in and INV are loaded before any use, v once
+// g, q and k have arrived: g, q, k and v as row pieces moved to the column-owner layout by
+// MFMA transposes, S_in and INV as 16-byte pieces (bf16: 16 x 32 blocks, written transposed
+// into LDS by MFMA transposes).
 template <class T, int K, int V, int C>
 __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
                                                        const T* __restrict__ vp, const float* __restrict__ gp,
