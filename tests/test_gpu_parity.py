@@ -45,6 +45,7 @@ SMALL = {
     "many_heads": small_workload("many_heads", B=1, T=200, H=72, HV=72, has_h0=True, has_dsf=True),
     "many_seqs": small_workload("many_seqs", H=4, HV=8, varlen=40, total=3000, len_lo=0, len_hi=150,
                                 has_h0=True, has_dsf=True),
+    "many_heads_c16": small_workload("many_heads_c16", B=1, T=90, H=72, HV=72, C=16, has_h0=True, has_dsf=True),
 }
 
 
@@ -94,7 +95,7 @@ def test_stage_parity_states_and_inverse(oracle_mod):
     assert e_states < 1e-2 and e_inv < 1e-2
 
 
-@pytest.mark.parametrize("name", ["varlen_edges", "gva3_varlen", "c16", "many_heads", "many_seqs"])
+@pytest.mark.parametrize("name", ["varlen_edges", "gva3_varlen", "c16", "many_heads", "many_seqs", "many_heads_c16"])
 def test_stage_parity_state_gradients(name):
     """Per-chunk state gradients of the reverse scan (the dS_out each chunk's products consume;
     FlashKDA backward page, step 2) against the fp64 chunked reference's, on packed ragged
