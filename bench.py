@@ -174,9 +174,27 @@ class Hip:
             self.lib.hipEventDestroy(e)
 
 
-def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True):
+def scan_forms_w(w, inp):
+    """Whether the reverse scan forms W itself (4 or more value slices per workgroup, the
+    library's scan_wq rule), so that the saved-operand backward launches no W kernel."""
+    slices = inp["N"] * w.HV * (w.V // 16)
+    nc = 1
+    while nc < w.V // 16 and slices // nc > 256:
+        nc *= 2
+    return w.dtype != "f32" and nc >= 4
+
+
+def saved_read_bytes(w, inp):
+    """Bytes of the forward's save that the saved-operand backward reads: kr, -w^T, Q'^T
+    (C x K each) and e^gam (K, fp32) per chunk-head."""
+    es = 4 if w.dtype == "f32" else 2
+    return num_chunks(w, inp) * w.HV * (3 * w.C * w.K * es + w.K * 4)
+
+
+def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True, saved=True):
     """Times kda_chunk_bwd on workload `wid`: cold and (optionally) warm call times, and the
-    per-kernel times from the library's event hook; optionally the forward with o."""
+    per-kernel times from the library's event hook; optionally the forward with o, and the
+    saved-operand pair (kda_fwd_states_save + kda_chunk_bwd_saved)."""
     import torch
     import chunked_gated_delta_09_amd as kda
     from chunked_gated_delta_09_amd import inputs as kin
@@ -202,17 +220,18 @@ def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True):
     dh0 = torch.empty(inp["N"], w.HV, w.K, w.V, dtype=torch.float32, device=dev)
     ws = torch.empty(kda.bwd_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
-    nk = 4 if inp["cu_seqlens"] is not None else 3  # kernels per call
-    names = (["chunk_table"] if nk == 4 else []) + BWD_KERNELS
+    table = ["chunk_table"] if inp["cu_seqlens"] is not None else []
+    names = table + BWD_KERNELS
 
     def step():
         kda.chunk_bwd_into(dims, d["q"], d["k"], d["v"], d["g"], d["beta"], fw["states"], fw["inv"], d["dO"],
                            d["dS_final"], dq, dk, dv, dg, dbeta, dh0, ws, stream=stream)
 
-    def timed(nsteps, flush, per_kernel):
+    def timed(nsteps, flush, per_kernel, step=step, names=names):
         """nsteps calls; HIP events around each call on its stream, and (per_kernel) the
         library's events around each of its kernels. The timed region is bracketed by
         device synchronisation."""
+        nk = len(names)
         call_ev = hip.events(2 * nsteps)
         kern_ev = hip.events(2 * nk * nsteps) if per_kernel else None
         torch.cuda.synchronize()
@@ -268,7 +287,7 @@ def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True):
         res["fwd_calls"] = [hip.elapsed(fwd_ev[2 * i], fwd_ev[2 * i + 1]) for i in range(steps)]
         hip.destroy(fwd_ev)
         # per-kernel times of the same calls, from the library's events (separate passes)
-        fnames = (["chunk_table"] if nk == 4 else []) + FWD_KERNELS
+        fnames = table + FWD_KERNELS
         nf = len(fnames)
         fk_ev = hip.events(2 * nf * steps)
         torch.cuda.synchronize()
@@ -283,6 +302,33 @@ def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True):
         res["fwd_kern"] = {name: [hip.elapsed(fk_ev[2 * nf * i + 2 * j], fk_ev[2 * nf * i + 2 * j + 1])
                                   for i in range(steps)] for j, name in enumerate(fnames)}
         hip.destroy(fk_ev)
+    if saved:
+        # Saved-operand mode: the forward also keeps kr, -w^T, Q'^T and e^gam; the backward
+        # then runs without its prep kernel (a small W kernel where the scan takes W as seeds).
+        fs = kda.fwd_states(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], cu_seqlens=inp["cu_seqlens"],
+                            C=w.C, scale=inp["scale"], save=True)
+        snames = table + ([] if scan_forms_w(w, inp) else ["bwd_w"]) + ["bwd_scan", "bwd_grad"]
+
+        def sstep():
+            kda.chunk_bwd_into(dims, d["q"], d["k"], d["v"], d["g"], d["beta"], fs["states"], fs["inv"], d["dO"],
+                               d["dS_final"], dq, dk, dv, dg, dbeta, dh0, ws, stream=stream, saved=fs["saved"])
+
+        def sfwd():
+            return kda.fwd_states(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"],
+                                  cu_seqlens=inp["cu_seqlens"], C=w.C, scale=inp["scale"], save=True)
+
+        for _ in range(warmup):
+            sstep()
+        res["saved_calls"], _, _ = timed(steps, flush=True, per_kernel=False, step=sstep, names=snames)
+        _, res["saved_kern"], _ = timed(steps, flush=True, per_kernel=True, step=sstep, names=snames)
+        for _ in range(2):
+            sfwd()
+        res["saved_fwd_calls"], _, _ = timed(steps, flush=True, per_kernel=False, step=sfwd,
+                                             names=table + FWD_KERNELS)
+        _, res["saved_fwd_kern"], _ = timed(steps, flush=True, per_kernel=True, step=sfwd,
+                                            names=table + FWD_KERNELS)
+        res["saved_bytes"] = fs["saved"].numel()
+        del fs
     del keep, fw, d, ws
     torch.cuda.empty_cache()
     return res
@@ -317,6 +363,25 @@ def summarize(res):
                           "algorithmic_bytes": fb, "achieved_GBps": fb / (fms * 1e-3) / 1e9,
                           "hbm_frac": fb / (fms * 1e-3) / PEAK_HBM_BYTES,
                           "kernels_ms_cold": {k: statistics.median(v) for k, v in res.get("fwd_kern", {}).items()}}
+    if "saved_calls" in res:
+        bms = statistics.median(res["saved_calls"])
+        fsms = statistics.median(res["saved_fwd_calls"])
+        sb = abytes + saved_read_bytes(w, inp)
+        blk = {"entries": "kda_fwd_states_save (forward with o, keeping kr, -w^T, Q'^T, e^gam) + "
+                          "kda_chunk_bwd_saved",
+               "bwd_ms_cold_median": bms, "bwd_token_heads_per_s": th / (bms * 1e-3),
+               "bwd_kernels_ms_cold": {k: statistics.median(v) for k, v in res["saved_kern"].items()},
+               "bwd_algorithmic_bytes": sb,
+               "bwd_algorithmic_bytes_note": "the call's own algorithmic bytes plus the save it reads",
+               "bwd_hbm_frac": sb / (bms * 1e-3) / PEAK_HBM_BYTES,
+               "fwd_ms_cold_median": fsms,
+               "fwd_kernels_ms_cold": {k: statistics.median(v) for k, v in res["saved_fwd_kern"].items()},
+               "saved_bytes": res["saved_bytes"]}
+        if "fwd_calls" in res:
+            fms = statistics.median(res["fwd_calls"])
+            blk["training_step_ms"] = {"recompute (kda_fwd_states with o + kda_chunk_bwd)": fms + ms,
+                                       "saved operands": fsms + bms}
+        out["saved_mode"] = blk
     return out
 
 
@@ -408,6 +473,7 @@ def main():
         "kernels_ms_cold": s["kernels_ms_cold"],
         "kernels_ms_warm": s["kernels_ms_warm"],
         "forward": s["forward"],
+        "saved_mode": s.get("saved_mode"),
         "per_workload": per_workload,
         "wall_s_timed_cold_incl_flush": main_res["cold_wall"],
     }

@@ -12,7 +12,7 @@ import math
 import os
 
 __all__ = ["load", "fwd_states", "chunk_bwd", "chunk_bwd_into", "chunk_bwd_noalloc_into", "make_dims", "num_chunks",
-           "fwd_workspace_bytes", "bwd_workspace_bytes", "KdaError", "LIB_PATH"]
+           "fwd_workspace_bytes", "bwd_workspace_bytes", "saved_bytes", "KdaError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -62,6 +62,12 @@ def load():
         lib.kda_chunk_bwd.argtypes = [dp] + [vp] * 15 + [vp, sz, vp]
         lib.kda_chunk_bwd_noalloc.restype = ctypes.c_int
         lib.kda_chunk_bwd_noalloc.argtypes = [dp] + [vp] * 15 + [vp]
+        lib.kda_saved_bytes.restype = sz
+        lib.kda_saved_bytes.argtypes = [dp]
+        lib.kda_fwd_states_save.restype = ctypes.c_int
+        lib.kda_fwd_states_save.argtypes = [dp] + [vp] * 10 + [vp, sz] + [vp, sz, vp]
+        lib.kda_chunk_bwd_saved.restype = ctypes.c_int
+        lib.kda_chunk_bwd_saved.argtypes = [dp] + [vp] * 8 + [sz] + [vp] * 8 + [vp, sz, vp]
         _lib = lib
     return _lib
 
@@ -104,6 +110,11 @@ def bwd_workspace_bytes(dims):
     return int(load().kda_bwd_workspace_bytes(ctypes.byref(dims)))
 
 
+def saved_bytes(dims):
+    """Bytes of the forward's save for the saved-operand backward (kda_saved_bytes)."""
+    return int(load().kda_saved_bytes(ctypes.byref(dims)))
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -143,10 +154,12 @@ def _geometry(q_or_k, v, C, cu_seqlens, scale, beta_logits=False):
 
 
 def fwd_states(q, k, v, g, beta, h0=None, cu_seqlens=None, C=64, scale=None, output_o=False,
-               output_final_state=True, beta_logits=False):
+               output_final_state=True, beta_logits=False, save=False):
     """Forward chunk states. Returns dict(states [NT,HV,K,V], inv [NT,HV,C,C],
-    final_state [N,HV,K,V] fp32 or None, o [B,T,HV,V] or None). ``beta_logits``: beta
-    holds logits (the kernels apply a sigmoid)."""
+    final_state [N,HV,K,V] fp32 or None, o [B,T,HV,V] or None, saved uint8 or None).
+    ``beta_logits``: beta holds logits (the kernels apply a sigmoid). ``save``: also keep the
+    backward's chunk operands (kda_fwd_states_save; implies output_o) for
+    ``chunk_bwd(..., saved=...)``."""
     import torch
     dims, keep, (B, T, H, HV, K, V, N) = _geometry(k, v, C, cu_seqlens, scale, beta_logits)
     tdt = k.dtype
@@ -162,20 +175,34 @@ def fwd_states(q, k, v, g, beta, h0=None, cu_seqlens=None, C=64, scale=None, out
     states = torch.empty(NT, HV, K, V, dtype=tdt, device=dev)
     inv = torch.empty(NT, HV, C, C, dtype=tdt, device=dev)
     final = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev) if output_final_state else None
-    o = torch.empty(B, T, HV, V, dtype=tdt, device=dev) if output_o else None
+    o = torch.empty(B, T, HV, V, dtype=tdt, device=dev) if (output_o or save) else None
     wsb = fwd_workspace_bytes(dims)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    _check(load().kda_fwd_states(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
-                                 _ptr(states), _ptr(inv), _ptr(final), _ptr(o), _ptr(ws), wsb, _stream()))
+    saved = None
+    if save:
+        svb = saved_bytes(dims)
+        saved = torch.empty(max(svb, 1), dtype=torch.uint8, device=dev)
+        _check(load().kda_fwd_states_save(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(h0), _ptr(states), _ptr(inv), _ptr(final), _ptr(o), _ptr(saved), svb,
+                                          _ptr(ws), wsb, _stream()))
+    else:
+        _check(load().kda_fwd_states(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                     _ptr(states), _ptr(inv), _ptr(final), _ptr(o), _ptr(ws), wsb, _stream()))
     del keep
-    return dict(states=states, inv=inv, final_state=final, o=o)
+    return dict(states=states, inv=inv, final_state=final, o=o, saved=saved)
 
 
 def chunk_bwd_into(dims, q, k, v, g, beta, states, inv, dO, dS_final, dq, dk, dv, dg, dbeta, dh0, workspace,
-                   stream=None):
+                   stream=None, saved=None):
     """Raw call with caller-owned outputs and workspace (no allocation, no checks beyond
-    the library's own)."""
+    the library's own). ``saved``: the forward's save (kda_chunk_bwd_saved)."""
     st = _stream() if stream is None else ctypes.c_void_p(stream)
+    if saved is not None:
+        _check(load().kda_chunk_bwd_saved(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(states), _ptr(inv), _ptr(saved), saved.numel(), _ptr(dO),
+                                          _ptr(dS_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
+                                          _ptr(dh0), _ptr(workspace), workspace.numel(), st))
+        return
     _check(load().kda_chunk_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(states),
                                 _ptr(inv), _ptr(dO), _ptr(dS_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
                                 _ptr(dbeta), _ptr(dh0), _ptr(workspace), workspace.numel(), st))
@@ -192,10 +219,11 @@ def chunk_bwd_noalloc_into(dims, q, k, v, g, beta, states, inv, dO, dS_final, dq
 
 
 def chunk_bwd(q, k, v, g, beta, states, inv, dO, dS_final=None, cu_seqlens=None, C=64, scale=None,
-              output_dh0=True, beta_logits=False):
+              output_dh0=True, beta_logits=False, saved=None):
     """Chunkwise backward. Returns dict(dq, dk [B,T,H,K], dv [B,T,HV,V], dg [B,T,HV,K] fp32,
     dbeta [B,T,HV] fp32, dh0 [N,HV,K,V] fp32 or None). ``beta_logits``: beta holds logits
-    and dbeta is the gradient w.r.t. them."""
+    and dbeta is the gradient w.r.t. them. ``saved``: the ``saved`` tensor of
+    ``fwd_states(..., save=True)`` on the same inputs (kda_chunk_bwd_saved)."""
     import torch
     dims, keep, (B, T, H, HV, K, V, N) = _geometry(q, v, C, cu_seqlens, scale, beta_logits)
     tdt = q.dtype
@@ -217,6 +245,8 @@ def chunk_bwd(q, k, v, g, beta, states, inv, dO, dS_final=None, cu_seqlens=None,
     dh0 = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev) if output_dh0 else None
     wsb = bwd_workspace_bytes(dims)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    chunk_bwd_into(dims, q, k, v, g, beta, states, inv, dO, dS_final, dq, dk, dv, dg, dbeta, dh0, ws)
+    if saved is not None:
+        _check_tensor(saved, "saved", torch.uint8, (max(saved_bytes(dims), 1),))
+    chunk_bwd_into(dims, q, k, v, g, beta, states, inv, dO, dS_final, dq, dk, dv, dg, dbeta, dh0, ws, saved=saved)
     del keep
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0)

@@ -112,6 +112,10 @@ struct FwdLayout {
 struct BwdLayout {
   size_t choff, kr, nwT, bcT, eg, dS, yT, total;
 };
+// The forward's save for the backward (kda_fwd_states_save / kda_chunk_bwd_saved).
+struct SavedLayout {
+  size_t kr, nwT, qpT, eg, total;
+};
 
 // Elements per chunk-head of the scan's K x C operand: the bf16 path stores it in
 // fragment order, padded to whole 32-wide contraction steps.
@@ -146,6 +150,35 @@ BwdLayout bwd_layout(const kda_dims* d, const Plan& p) {
   L.yT = o; o = align_up(o + nth * p.V * p.C * p.es);
   L.total = o;
   return L;
+}
+
+SavedLayout saved_layout(const kda_dims* d, const Plan& p) {
+  SavedLayout L;
+  const size_t nth = (size_t)p.NT * d->HV;
+  size_t o = 0;
+  L.kr = o; o = align_up(o + nth * p.C * p.K * p.es);
+  L.nwT = o; o = align_up(o + nth * p2_elems(p) * p.es);
+  L.qpT = o; o = align_up(o + nth * p2_elems(p) * p.es);
+  L.eg = o; o = align_up(o + nth * p.K * sizeof(float));
+  L.total = o;
+  return L;
+}
+
+kda::SavedWs saved_ws(void* saved, const SavedLayout& L) {
+  char* b = static_cast<char*>(saved);
+  kda::SavedWs sv;
+  sv.kr = b + L.kr;
+  sv.nwT = b + L.nwT;
+  sv.qpT = b + L.qpT;
+  sv.eg = reinterpret_cast<float*>(b + L.eg);
+  return sv;
+}
+
+kda_status check_saved(const void* saved, size_t bytes, size_t need) {
+  if (saved == nullptr && need > 0) return fail(KDA_EINVAL, "saved is NULL (%zu bytes needed)", need);
+  if (bytes < need) return fail(KDA_EINVAL, "saved buffer too small: %zu bytes given, %zu needed", bytes, need);
+  if (reinterpret_cast<uintptr_t>(saved) % kAlign != 0) return fail(KDA_EINVAL, "saved must be 256-byte aligned");
+  return KDA_OK;
 }
 
 kda::Shape make_shape(const kda_dims* d, const Plan& p, void* ws, size_t choff_off) {
@@ -218,6 +251,12 @@ KDA_EXPORT size_t kda_bwd_workspace_bytes(const kda_dims* dims) {
   return bwd_layout(dims, p).total;
 }
 
+KDA_EXPORT size_t kda_saved_bytes(const kda_dims* dims) {
+  Plan p;
+  if (validate(dims, p, false) != KDA_OK) return 0;
+  return saved_layout(dims, p).total;
+}
+
 KDA_EXPORT const char* kda_last_error(void) { return g_err.c_str(); }
 
 KDA_EXPORT void kda_set_kernel_events(void* const* events, int count) {
@@ -225,9 +264,11 @@ KDA_EXPORT void kda_set_kernel_events(void* const* events, int count) {
   g_nevents = count > 0 ? count : 0;
 }
 
-KDA_EXPORT kda_status kda_fwd_states(const kda_dims* dims, const void* q, const void* k, const void* v,
-                                     const float* g, const float* beta, const void* h0, void* states, void* inv,
-                                     float* final_state, void* o, void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+
+kda_status fwd_impl(const kda_dims* dims, const void* q, const void* k, const void* v, const float* g,
+                    const float* beta, const void* h0, void* states, void* inv, float* final_state, void* o,
+                    void* saved, size_t saved_bytes, bool save, void* workspace, size_t ws_bytes, void* stream) {
   Plan p;
   kda_status st = validate(dims, p, true);
   if (st != KDA_OK) return st;
@@ -239,10 +280,19 @@ KDA_EXPORT kda_status kda_fwd_states(const kda_dims* dims, const void* q, const 
     KDA_REQUIRE(states, "states");
     KDA_REQUIRE(inv, "inv");
     if (o != nullptr) KDA_REQUIRE(q, "q (needed for o)");
+    if (save) {
+      KDA_REQUIRE(q, "q");
+      KDA_REQUIRE(o, "o (the save is written by the output kernel)");
+    }
   }
   const FwdLayout L = fwd_layout(dims, p);
   st = check_ws(workspace, ws_bytes, L.total);
   if (st != KDA_OK) return st;
+  const SavedLayout SL = saved_layout(dims, p);
+  if (save) {
+    st = check_saved(saved, saved_bytes, SL.total);
+    if (st != KDA_OK) return st;
+  }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   LaunchCounter lc(hs);
   char* ws = static_cast<char*>(workspace);
@@ -252,17 +302,39 @@ KDA_EXPORT kda_status kda_fwd_states(const kda_dims* dims, const void* q, const 
   fw.krT = ws + L.krT;
   fw.uT = ws + L.uT;
   fw.eg = reinterpret_cast<float*>(ws + L.eg);
+  kda::SavedWs sv{};
+  if (save) sv = saved_ws(saved, SL);
+  const kda::SavedWs* svp = save ? &sv : nullptr;
   if (p.varlen) KDA_HIP(kda::launch_chunk_offsets(dims->cu_seqlens_dev, dims->N, p.C, reinterpret_cast<int32_t*>(ws + L.choff), hs));
-  KDA_HIP(kda::launch_fwd_prep(p.dtype, p.C, s, k, v, g, beta, inv, fw, hs));
+  KDA_HIP(kda::launch_fwd_prep(p.dtype, p.C, s, k, v, g, beta, inv, fw, hs, svp));
   KDA_HIP(kda::launch_scan_fwd(p.dtype, p.C, s, fw, h0, states, final_state, hs));
-  if (o != nullptr) KDA_HIP(kda::launch_fwd_out(p.dtype, p.C, s, q, k, v, g, beta, states, inv, o, hs));
+  if (o != nullptr) KDA_HIP(kda::launch_fwd_out(p.dtype, p.C, s, q, k, v, g, beta, states, inv, o, hs, svp));
   return KDA_OK;
 }
 
-KDA_EXPORT kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const void* k, const void* v,
-                                    const float* g, const float* beta, const void* states, const void* inv,
-                                    const void* dO, const void* dS_final, void* dq, void* dk, void* dv, float* dg,
-                                    float* dbeta, float* dh0, void* workspace, size_t ws_bytes, void* stream) {
+}  // namespace
+
+KDA_EXPORT kda_status kda_fwd_states(const kda_dims* dims, const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta, const void* h0, void* states, void* inv,
+                                     float* final_state, void* o, void* workspace, size_t ws_bytes, void* stream) {
+  return fwd_impl(dims, q, k, v, g, beta, h0, states, inv, final_state, o, nullptr, 0, false, workspace, ws_bytes,
+                  stream);
+}
+
+KDA_EXPORT kda_status kda_fwd_states_save(const kda_dims* dims, const void* q, const void* k, const void* v,
+                                          const float* g, const float* beta, const void* h0, void* states, void* inv,
+                                          float* final_state, void* o, void* saved, size_t saved_bytes,
+                                          void* workspace, size_t ws_bytes, void* stream) {
+  return fwd_impl(dims, q, k, v, g, beta, h0, states, inv, final_state, o, saved, saved_bytes, true, workspace,
+                  ws_bytes, stream);
+}
+
+namespace {
+
+kda_status bwd_impl(const kda_dims* dims, const void* q, const void* k, const void* v, const float* g,
+                    const float* beta, const void* states, const void* inv, const void* saved, size_t saved_bytes,
+                    bool use_saved, const void* dO, const void* dS_final, void* dq, void* dk, void* dv, float* dg,
+                    float* dbeta, float* dh0, void* workspace, size_t ws_bytes, void* stream) {
   Plan p;
   kda_status st = validate(dims, p, true);
   if (st != KDA_OK) return st;
@@ -284,6 +356,11 @@ KDA_EXPORT kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const v
   const BwdLayout L = bwd_layout(dims, p);
   st = check_ws(workspace, ws_bytes, L.total);
   if (st != KDA_OK) return st;
+  const SavedLayout SL = saved_layout(dims, p);
+  if (use_saved) {
+    st = check_saved(saved, saved_bytes, SL.total);
+    if (st != KDA_OK) return st;
+  }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   LaunchCounter lc(hs);
   char* ws = static_cast<char*>(workspace);
@@ -296,10 +373,44 @@ KDA_EXPORT kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const v
   bw.dS = ws + L.dS;
   bw.yT = ws + L.yT;
   if (p.varlen) KDA_HIP(kda::launch_chunk_offsets(dims->cu_seqlens_dev, dims->N, p.C, reinterpret_cast<int32_t*>(ws + L.choff), hs));
-  KDA_HIP(kda::launch_bwd_prep(p.dtype, p.C, s, q, k, g, beta, inv, dO, bw, hs));
+  if (use_saved) {
+    // the scan reads the forward's kr, -w^T and e^gam; W comes from the saved Q'^T, formed
+    // by the scan itself or by a small kernel into the workspace
+    const kda::SavedWs sv = saved_ws(const_cast<void*>(saved), SL);
+    bw.kr = sv.kr;
+    bw.nwT = sv.nwT;
+    bw.eg = sv.eg;
+    if (kda::scan_wq(p.dtype, s, p.V)) {
+      bw.bcT = sv.qpT;
+    } else {
+      KDA_HIP(kda::launch_bwd_w(p.dtype, p.C, s, dO, sv, bw, hs));
+    }
+  } else {
+    KDA_HIP(kda::launch_bwd_prep(p.dtype, p.C, s, q, k, g, beta, inv, dO, bw, hs));
+  }
   KDA_HIP(kda::launch_scan_bwd(p.dtype, p.C, s, bw, dO, dS_final, dh0, hs));
   KDA_HIP(kda::launch_bwd_grad(p.dtype, p.C, s, q, k, v, g, beta, states, inv, dO, bw, dq, dk, dv, dg, dbeta, hs));
   return KDA_OK;
+}
+
+}  // namespace
+
+KDA_EXPORT kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta, const void* states, const void* inv,
+                                    const void* dO, const void* dS_final, void* dq, void* dk, void* dv, float* dg,
+                                    float* dbeta, float* dh0, void* workspace, size_t ws_bytes, void* stream) {
+  return bwd_impl(dims, q, k, v, g, beta, states, inv, nullptr, 0, false, dO, dS_final, dq, dk, dv, dg, dbeta, dh0,
+                  workspace, ws_bytes, stream);
+}
+
+KDA_EXPORT kda_status kda_chunk_bwd_saved(const kda_dims* dims, const void* q, const void* k, const void* v,
+                                          const float* g, const float* beta, const void* states, const void* inv,
+                                          const void* saved, size_t saved_bytes, const void* dO,
+                                          const void* dS_final, void* dq, void* dk, void* dv, float* dg,
+                                          float* dbeta, float* dh0, void* workspace, size_t ws_bytes,
+                                          void* stream) {
+  return bwd_impl(dims, q, k, v, g, beta, states, inv, saved, saved_bytes, true, dO, dS_final, dq, dk, dv, dg, dbeta,
+                  dh0, workspace, ws_bytes, stream);
 }
 
 KDA_EXPORT kda_status kda_bwd_state_grads(const kda_dims* dims, const void* workspace, size_t ws_bytes,

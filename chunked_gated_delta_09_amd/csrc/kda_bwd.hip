@@ -244,7 +244,7 @@ __global__ __launch_bounds__(512, 4) void bwd_prep_kernel(Shape s, const T* __re
           for (int j = 0; j < 4; ++j) qp4[j] = to_f(QL[(16 * mt + 4 * grp + j) * LDK + col]) * eR - acc[jb][j];
           if constexpr (QPT) {
             static_assert(sizeof(T) == 2 && ScanFrag<K, V, C>::P2_ELEMS <= V * K, "Q'^T fits the W buffer");
-            st4(reinterpret_cast<T*>(ws.bcT) + ch * V * K + ScanFrag<K, V, C>::p2(col, 16 * mt + 4 * grp), qp4);
+            st4(reinterpret_cast<T*>(ws.bcT) + ch * ScanFrag<K, V, C>::P2_ELEMS + ScanFrag<K, V, C>::p2(col, 16 * mt + 4 * grp), qp4);
           } else {
             st4(QpT + col * LDC + 16 * mt + 4 * grp, qp4);
           }
@@ -1084,6 +1084,118 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     }
   }
   KDA_TS(2, 9);
+}
+
+// W = Q'^T dO for the saved path (kda_chunk_bwd_saved): the tail of the prep kernel, with
+// Q'^T read back from the forward's save in the scan's fragment order. One workgroup per
+// (chunk, value head); dO^T staged in LDS; wave w owns the K rows 16w .. of W. It also pulls
+// the chunk's saved kr, -w^T and e^gam into the caches (copies to a scratch LDS block that
+// nothing reads): the reverse scan that follows is a chain of dependent steps whose operand
+// copies otherwise come from HBM.
+template <class T, int K, int V, int C>
+__global__ __launch_bounds__(512) void bwd_w_kernel(Shape s, const T* __restrict__ dOp, SavedWs saved, BwdWs ws) {
+  constexpr int NW = 8, RT = C / 16, KT = K / 16, VT = V / 16, NCV = (VT + NW - 1) / NW;
+  constexpr int LDC = C + pad_of<T>();
+  __shared__ __align__(16) T DoT[V * LDC];
+  __shared__ __align__(16) unsigned char land[sizeof(T) == 2 ? NW * 1024 : 16];
+  const int task = group_task(blockIdx.x, s.HV / s.H, s.NT * s.nhv);
+  if (task < 0) return;
+  const int c = task / s.nhv, h = s.hv0 + task % s.nhv;
+  const Geo geo = chunk_geo(c, s.cu, s.choff, s.N, s.T, C);
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long ch = (long)c * s.HV + h;
+  const int len = geo.len;
+  if (len <= 0) return;
+  const int vs = s.HV * V;
+  const T* __restrict__ dOc = dOp + (geo.bos * s.HV + h) * V;
+  typedef ScanFrag<K, V, C> SF;
+  // this wave's A fragments of Q'^T (K tile `wave`), requested first
+  bf16x8 af[sizeof(T) == 2 ? SF::CQ : 1];
+  if constexpr (sizeof(T) == 2) {
+    static_assert(KT == NW, "one K tile per wave");
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(saved.qpT) + ch * (SF::P2_ELEMS / 8) + lane;
+#pragma unroll
+    for (int q = 0; q < SF::CQ; ++q) af[q] = src[(wave * SF::CQ + q) * 64];
+    // the scan's operands of this chunk-head: 1 KB blocks of kr and -w^T shared out over the
+    // waves, and e^gam
+    constexpr int NB1 = SF::P1_ELEMS / 512, NB2 = SF::P2_ELEMS / 512, PER = (NB1 + NB2 + NW - 1) / NW;
+    const bf16* kr = reinterpret_cast<const bf16*>(saved.kr) + ch * SF::P1_ELEMS + 8 * lane;
+    const bf16* nw = reinterpret_cast<const bf16*>(saved.nwT) + ch * SF::P2_ELEMS + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int b = wave * PER + i;
+      if (b < NB1) copy16_to_lds(kr + 512 * b, land + 1024 * wave);
+      else if (b < NB1 + NB2) copy16_to_lds(nw + 512 * (b - NB1), land + 1024 * wave);
+    }
+    if (wave == 0) copy16_to_lds(saved.eg + ch * K + 4 * (lane % (K / 4)), land);
+  }
+  // dO^T (rows past the chunk's end as zero): row pieces moved to the column-owner layout
+  ColTile<T, RT> td[NCV];
+#pragma unroll
+  for (int cv = 0; cv < NCV; ++cv) td[cv].load(dOc, vs, 16 * min(wave + cv * NW, VT - 1), lane, len);
+#pragma unroll
+  for (int cv = 0; cv < NCV; ++cv) {
+    float x[RT][4];
+    td[cv].get(x, lane, len);
+    const int vt = wave + cv * NW;
+    if (vt < VT) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        st4(DoT + (16 * vt + n) * LDC + 16 * rt + 4 * grp, f32x4{x[rt][0], x[rt][1], x[rt][2], x[rt][3]});
+    }
+  }
+  __syncthreads();
+  T* __restrict__ bcT = reinterpret_cast<T*>(ws.bcT) + ch * V * K;
+  if constexpr (sizeof(T) == 2) {
+    const int kt = wave;
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int q = 0; q < SF::CQ; ++q) {
+        // B: dO rows in the fragment order's contraction order (32q + 4grp .. +3, then
+        // 32q + 16 + 4grp .. +3) of column 16vt + n; the second half is absent when C = 16
+        const bool pair2 = 2 * q + 1 < RT;
+        const T* br = DoT + (16 * vt + n) * LDC + 32 * q + 4 * grp;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(br);
+        bf16x4 hi = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+        if (pair2) hi = *reinterpret_cast<const bf16x4*>(br + 16);
+        const bf16x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        bf16x8 a = af[q];
+        if (!pair2) {  // the fragment order pads C = 16 to a 32-wide step: unwritten there
+#pragma unroll
+          for (int i = 4; i < 8; ++i) a[i] = (bf16)0.0f;
+        }
+        acc = Mma<T>::mma(a, b, acc);
+      }
+      // column v = 16vt + n goes to its scan slice and lane
+      const int v = 16 * vt + n;
+      st4(bcT + SF::seed(ScanCols::slice(v), kt, KT, ScanCols::lane_col(v) + 16 * grp), acc);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the cache pulls have landed
+  } else {
+    const T* __restrict__ qps = reinterpret_cast<const T*>(saved.qpT) + ch * K * C;
+    for (int e = tid; e < K * V; e += 64 * NW) {
+      const int k = e / V, v = e % V;
+      float acc = 0.f;
+      for (int j = 0; j < C; ++j) acc += to_f(qps[k * C + j]) * to_f(DoT[v * LDC + j]);
+      bcT[v * K + k] = from_f<T>(acc);
+    }
+  }
+}
+
+hipError_t launch_bwd_w(int dtype, int C, const Shape& s, const void* dO, const SavedWs& sv, const BwdWs& ws,
+                        hipStream_t st) {
+  if (s.NT == 0) return hipSuccess;
+  const dim3 grid(group_grid(s.NT * s.nhv, s.HV / s.H)), block(512);
+  if (dtype == 0)
+    hipLaunchKernelGGL((bwd_w_kernel<float, 16, 16, 16>), grid, block, 0, st, s, static_cast<const float*>(dO), sv, ws);
+  else if (C == 64)
+    hipLaunchKernelGGL((bwd_w_kernel<bf16, 128, 128, 64>), grid, block, 0, st, s, static_cast<const bf16*>(dO), sv, ws);
+  else
+    hipLaunchKernelGGL((bwd_w_kernel<bf16, 128, 128, 16>), grid, block, 0, st, s, static_cast<const bf16*>(dO), sv, ws);
+  return hipGetLastError();
 }
 
 template <class T, int K, int V, int C>

@@ -535,6 +535,21 @@ struct ScanFrag {
   }
 };
 
+// Global -> LDS copies (lane i's bytes land at lds + i * bytes). Issued as inline assembly:
+// the compiler's wait insertion would otherwise treat every LDS read of a buffer they fill
+// as depending on these copies and make the reading wave wait for all of its own outstanding
+// global stores. The copying wave waits for its copies explicitly (vmcnt) before a barrier
+// hands them over, and before the workgroup ends.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+__device__ __forceinline__ void copy16_to_lds(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory", "m0");
+}
+
 // Columns of the backward scan's column slices. Slice vt, lane column n, holds value
 // column col(vt, n): slices 2m and 2m+1 share the 32 columns 32m.., each taking 4 of every
 // 8. After a 16 x 16 transpose the 4 values a lane holds of slice 2m and those of slice

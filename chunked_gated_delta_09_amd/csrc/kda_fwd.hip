@@ -128,11 +128,12 @@ __device__ __forceinline__ void unit_lower_inverse(const float* __restrict__ L, 
   }
 }
 
-// One workgroup per (chunk, value head); 512 threads, two workgroups per CU.
-template <class T, int K, int V, int C>
+// One workgroup per (chunk, value head); 512 threads, two workgroups per CU. SAVE: also writes
+// the backward's kr, -w^T (the reverse scan's fragment orders) and e^gam to `saved`.
+template <class T, int K, int V, int C, bool SAVE>
 __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __restrict__ kp, const T* __restrict__ vp,
                                                            const float* __restrict__ gp, const float* __restrict__ bp,
-                                                           T* __restrict__ invp, FwdWs ws) {
+                                                           T* __restrict__ invp, FwdWs ws, SavedWs saved) {
   typedef FwdPrepLds<T, K, V, C> Lay;
   constexpr int NW = 8, RT = C / 16, KT = K / 16, VT = V / 16;
   static_assert(NW <= 8, "one reference-mode flag per wave");
@@ -219,8 +220,22 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
         } else {
           st4(krT + col * C + 16 * rt + 4 * grp, kr4);
         }
+        if constexpr (SAVE) {
+          // kr for the reverse scan, [C][K] in its fragment order (row pieces: this lane row
+          // 16rt + n, columns 16kt + 4grp ..)
+          T* __restrict__ krs = reinterpret_cast<T*>(saved.kr) + ch * C * K;
+          if constexpr (sizeof(T) == 2) {
+            st4(krs + ScanFrag<K, V, C>::p1(16 * rt + n, 16 * kt + 4 * grp), to_rows_bf16(kr4[0], kr4[1], kr4[2], kr4[3], lane));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) krs[(16 * rt + 4 * grp + j) * K + col] = kr4[j];
+          }
+        }
       }
-      if (grp == 0) ws.eg[ch * K + col] = __expf(gam);
+      if (grp == 0) {
+        ws.eg[ch * K + col] = __expf(gam);
+        if constexpr (SAVE) saved.eg[ch * K + col] = __expf(gam);
+      }
     }
   }
   if (lane == 0) wflag[wave] = strong_w;
@@ -285,6 +300,18 @@ __global__ __launch_bounds__(512, 2) void fwd_prep_kernel(Shape s, const T* __re
         } else {
           st4(negw + (16 * nt0 + n) * K + 16 * mt + 4 * grp, -acc[0]);
         }
+        if constexpr (SAVE) {
+          // -w^T for the reverse scan, [K][C] in its fragment order: the tile moved to the row
+          // layout (this lane: k = 16mt + n, c = 16nt0 + 4grp ..)
+          T* __restrict__ nws = reinterpret_cast<T*>(saved.nwT) + ch * (sizeof(T) == 2 ? ScanFrag<K, V, C>::P2_ELEMS : K * C);
+          if constexpr (sizeof(T) == 2) {
+            st4(nws + ScanFrag<K, V, C>::p2(16 * mt + n, 16 * nt0 + 4 * grp),
+                to_rows_bf16(-acc[0][0], -acc[0][1], -acc[0][2], -acc[0][3], lane));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) nws[(16 * mt + 4 * grp + j) * C + 16 * nt0 + n] = -acc[0][j];
+          }
+        }
       }, wave, lane);
   // u = INV diag(beta) v, stored transposed [V][C].
   T* uT = reinterpret_cast<T*>(ws.uT) + ch * V * C;
@@ -327,12 +354,14 @@ struct FwdOutLds {
 // (chunk, value head), 512 threads. g, q, k, S_in and INV are loaded before any use, v once
 // g, q and k have arrived: g, q, k and v as row pieces moved to the column-owner layout by
 // MFMA transposes, S_in and INV as 16-byte pieces (bf16: 16 x 32 blocks, written transposed
-// into LDS by MFMA transposes).
-template <class T, int K, int V, int C>
+// into LDS by MFMA transposes). SAVE: also writes the backward's Q'^T = (qd - Mqk w)^T to
+// `saved` (the reverse scan's fragment order), from qd and Mqk in LDS and the -w^T that the
+// prep kernel saved.
+template <class T, int K, int V, int C, bool SAVE>
 __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restrict__ qp, const T* __restrict__ kp,
                                                        const T* __restrict__ vp, const float* __restrict__ gp,
                                                        const float* __restrict__ bp, const T* __restrict__ states,
-                                                       const T* __restrict__ invp, T* __restrict__ op) {
+                                                       const T* __restrict__ invp, T* __restrict__ op, SavedWs saved) {
   typedef FwdOutLds<T, K, V, C> Lay;
   typedef T vecT __attribute__((ext_vector_type(16 / sizeof(T))));
   typedef T t4 __attribute__((ext_vector_type(4)));
@@ -550,6 +579,17 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
         store_rows<T>(Mqk, LDC, 16 * mt, 16 * nt0, m4, lane, 1 << 30);
       }, wave, lane);
   __syncthreads();
+  // SAVE, bf16: the saved -w^T fragments of this wave's K column tile (16 x 32 steps of the
+  // scan's fragment order, which are the B fragments of -w), requested here to land during
+  // the products below
+  typedef ScanFrag<K, V, C> SF;
+  bf16x8 nwf[SAVE && sizeof(T) == 2 ? SF::CQ : 1];
+  if constexpr (SAVE && sizeof(T) == 2) {
+    static_assert(SF::KT == NW, "one K column tile per wave");
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(saved.nwT) + ch * (SF::P2_ELEMS / 8) + lane;
+#pragma unroll
+    for (int q = 0; q < SF::CQ; ++q) nwf[q] = src[(wave * SF::CQ + q) * 64];
+  }
   // ---- U = INV vcorr, stored transposed
   block_gemm<T, RT, VT, BN, NW, C>(
       INVt, LDC, 1 << 30, VcT, LDC, [](int mt, int, int& kb, int& ke) { ke = min(C, round_up<T>(16 * (mt + 1))); },
@@ -566,6 +606,48 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Shape s, const T* __restri
 #pragma unroll
         for (int jb = 0; jb < BN; ++jb) store_rows<T>(oc, vs, 16 * mt, 16 * (nt0 + jb), acc[jb], lane, len);
       }, wave, lane);
+  if constexpr (SAVE) {
+    // Q' = qd + Mqk (-w) (Qd and Mqk are still in LDS: the products above only read them),
+    // stored transposed in the scan's K x C fragment order
+    if constexpr (sizeof(T) == 2) {
+      T* __restrict__ qps = reinterpret_cast<T*>(saved.qpT) + ch * SF::P2_ELEMS;
+      const int kt = wave;
+#pragma unroll
+      for (int mt = 0; mt < RT; ++mt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int q = 0; q < SF::CQ; ++q) {
+          // A: Mqk rows 16mt + n, columns in the fragment order's contraction order (32q + 4grp
+          // .. +3, then 32q + 16 + 4grp .. +3); the second half is absent when C = 16
+          const bool pair2 = 2 * q + 1 < RT;
+          const T* mr = Mqk + (16 * mt + n) * LDC + 32 * q + 4 * grp;
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(mr);
+          bf16x4 hi = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+          if (pair2) hi = *reinterpret_cast<const bf16x4*>(mr + 16);
+          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          bf16x8 b = nwf[q];
+          if (!pair2) {  // the fragment order pads C = 16 to a 32-wide step: unwritten there
+#pragma unroll
+            for (int i = 4; i < 8; ++i) b[i] = (bf16)0.0f;
+          }
+          acc = Mma<T>::mma(a, b, acc);
+        }
+        f32x4 qp4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qp4[j] = to_f(Qd[(16 * mt + 4 * grp + j) * LDK + 16 * kt + n]) + acc[j];
+        st4(qps + SF::p2(16 * kt + n, 16 * mt + 4 * grp), qp4);
+      }
+    } else {
+      const T* __restrict__ nws = reinterpret_cast<const T*>(saved.nwT) + ch * K * C;
+      T* __restrict__ qps = reinterpret_cast<T*>(saved.qpT) + ch * K * C;
+      for (int e = tid; e < C * K; e += NTH) {
+        const int r = e / K, k = e % K;
+        float acc = to_f(Qd[r * LDK + k]);
+        for (int j = 0; j < C; ++j) acc += to_f(Mqk[r * LDC + j]) * to_f(nws[k * C + j]);
+        qps[k * C + r] = from_f<T>(acc);
+      }
+    }
+  }
 }
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int C, int32_t* choff, hipStream_t st) {
@@ -575,36 +657,48 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int C, int32_t* choff,
 
 template <class T, int K, int V, int C>
 static hipError_t fwd_prep_t(const Shape& s, const void* k, const void* v, const float* g, const float* beta,
-                             void* inv, const FwdWs& ws, hipStream_t st) {
+                             void* inv, const FwdWs& ws, hipStream_t st, const SavedWs* sv) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_prep_kernel<T, K, V, C>), dim3(group_grid(s.NT * s.nhv, s.HV / s.H)), dim3(512), 0, st, s,
-                     static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<T*>(inv), ws);
+  const dim3 grid(group_grid(s.NT * s.nhv, s.HV / s.H)), block(512);
+  if (sv != nullptr)
+    hipLaunchKernelGGL((fwd_prep_kernel<T, K, V, C, true>), grid, block, 0, st, s, static_cast<const T*>(k),
+                       static_cast<const T*>(v), g, beta, static_cast<T*>(inv), ws, *sv);
+  else
+    hipLaunchKernelGGL((fwd_prep_kernel<T, K, V, C, false>), grid, block, 0, st, s, static_cast<const T*>(k),
+                       static_cast<const T*>(v), g, beta, static_cast<T*>(inv), ws, SavedWs{});
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_prep(int dtype, int C, const Shape& s, const void* k, const void* v, const float* g,
-                           const float* beta, void* inv, const FwdWs& ws, hipStream_t st) {
-  if (dtype == 0) return fwd_prep_t<float, 16, 16, 16>(s, k, v, g, beta, inv, ws, st);
-  if (C == 64) return fwd_prep_t<bf16, 128, 128, 64>(s, k, v, g, beta, inv, ws, st);
-  return fwd_prep_t<bf16, 128, 128, 16>(s, k, v, g, beta, inv, ws, st);
+                           const float* beta, void* inv, const FwdWs& ws, hipStream_t st, const SavedWs* sv) {
+  if (dtype == 0) return fwd_prep_t<float, 16, 16, 16>(s, k, v, g, beta, inv, ws, st, sv);
+  if (C == 64) return fwd_prep_t<bf16, 128, 128, 64>(s, k, v, g, beta, inv, ws, st, sv);
+  return fwd_prep_t<bf16, 128, 128, 16>(s, k, v, g, beta, inv, ws, st, sv);
 }
 
 template <class T, int K, int V, int C>
 static hipError_t fwd_out_t(const Shape& s, const void* q, const void* k, const void* v, const float* g,
-                            const float* beta, const void* states, const void* inv, void* o, hipStream_t st) {
+                            const float* beta, const void* states, const void* inv, void* o, hipStream_t st,
+                            const SavedWs* sv) {
   if (s.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_out_kernel<T, K, V, C>), dim3(group_grid(s.NT * s.nhv, s.HV / s.H)), dim3(512), 0, st, s,
-                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), g, beta,
-                     static_cast<const T*>(states), static_cast<const T*>(inv), static_cast<T*>(o));
+  const dim3 grid(group_grid(s.NT * s.nhv, s.HV / s.H)), block(512);
+  if (sv != nullptr)
+    hipLaunchKernelGGL((fwd_out_kernel<T, K, V, C, true>), grid, block, 0, st, s, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<const T*>(states),
+                       static_cast<const T*>(inv), static_cast<T*>(o), *sv);
+  else
+    hipLaunchKernelGGL((fwd_out_kernel<T, K, V, C, false>), grid, block, 0, st, s, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), g, beta, static_cast<const T*>(states),
+                       static_cast<const T*>(inv), static_cast<T*>(o), SavedWs{});
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_out(int dtype, int C, const Shape& s, const void* q, const void* k, const void* v,
                           const float* g, const float* beta, const void* states, const void* inv, void* o,
-                          hipStream_t st) {
-  if (dtype == 0) return fwd_out_t<float, 16, 16, 16>(s, q, k, v, g, beta, states, inv, o, st);
-  if (C == 64) return fwd_out_t<bf16, 128, 128, 64>(s, q, k, v, g, beta, states, inv, o, st);
-  return fwd_out_t<bf16, 128, 128, 16>(s, q, k, v, g, beta, states, inv, o, st);
+                          hipStream_t st, const SavedWs* sv) {
+  if (dtype == 0) return fwd_out_t<float, 16, 16, 16>(s, q, k, v, g, beta, states, inv, o, st, sv);
+  if (C == 64) return fwd_out_t<bf16, 128, 128, 64>(s, q, k, v, g, beta, states, inv, o, st, sv);
+  return fwd_out_t<bf16, 128, 128, 16>(s, q, k, v, g, beta, states, inv, o, st, sv);
 }
 
 }  // namespace kda

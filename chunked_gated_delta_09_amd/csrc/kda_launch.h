@@ -29,12 +29,23 @@ struct FwdWs {
   float* eg;   // [K]      e^gam
 };
 
+// Per-chunk tensors the forward can save for the backward (all [NT, HV, ...]; bf16 path in the
+// reverse scan's fragment order, ScanFrag): what the backward's prep kernel would otherwise
+// recompute from q, k, g, beta and INV.
+struct SavedWs {
+  void* kr;    // [C][K]   k e^(gam-G)
+  void* nwT;   // [K][C]   -w^T
+  void* qpT;   // [K][C]   Q'^T, Q' = qd - Mqk w
+  float* eg;   // [K]      e^gam
+};
+
 // Per-chunk workspace tensors of the backward (all [NT, HV, ...]).
 struct BwdWs {
   void* kr;    // [C][K]   k e^(gam-G)
   void* nwT;   // [K][C]   -w^T
   void* bcT;   // [V][K]   W = Q'^T dO, transposed (Q' = qd - Mqk w); or, where the scan forms W
-               //          itself (scan_wq), Q'^T [K][C] in the scan's fragment order
+               //          itself (scan_wq), Q'^T [K][C] in the scan's fragment order (a
+               //          chunk-head every ScanFrag::P2_ELEMS elements)
   float* eg;   // [K]      e^gam
   void* dS;    // [K][V]   gradient w.r.t. each chunk's S_out
   void* yT;    // [V][C]   (kr dS)^T
@@ -56,17 +67,23 @@ inline bool scan_wq(int dtype, const Shape& s, int V) { return dtype != 0 && sca
 
 // dtype: 0 = fp32 (K = V = C = 16), 1 = bf16 (K = V = 128, C in {16, 64}).
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int C, int32_t* choff, hipStream_t st);
+// sv: where to save the backward's chunk operands (nullptr: not saved).
 hipError_t launch_fwd_prep(int dtype, int C, const Shape& s, const void* k, const void* v, const float* g,
-                           const float* beta, void* inv, const FwdWs& ws, hipStream_t st);
+                           const float* beta, void* inv, const FwdWs& ws, hipStream_t st,
+                           const SavedWs* sv = nullptr);
 hipError_t launch_fwd_out(int dtype, int C, const Shape& s, const void* q, const void* k, const void* v,
                           const float* g, const float* beta, const void* states, const void* inv, void* o,
-                          hipStream_t st);
+                          hipStream_t st, const SavedWs* sv = nullptr);
 hipError_t launch_scan_fwd(int dtype, int C, const Shape& s, const FwdWs& ws, const void* h0, void* states,
                            float* final_state, hipStream_t st);
 hipError_t launch_bwd_prep(int dtype, int C, const Shape& s, const void* q, const void* k, const float* g,
                            const float* beta, const void* inv, const void* dO, const BwdWs& ws, hipStream_t st);
 hipError_t launch_scan_bwd(int dtype, int C, const Shape& s, const BwdWs& ws, const void* dO, const void* dSf,
                            float* dh0, hipStream_t st);
+// W = Q'^T dO from the saved Q'^T into ws.bcT, in the scan's seed order (the part of the
+// backward prep kernel that needs dO).
+hipError_t launch_bwd_w(int dtype, int C, const Shape& s, const void* dO, const SavedWs& sv, const BwdWs& ws,
+                        hipStream_t st);
 hipError_t launch_bwd_grad(int dtype, int C, const Shape& s, const void* q, const void* k, const void* v,
                            const float* g, const float* beta, const void* states, const void* inv, const void* dO,
                            const BwdWs& ws, void* dq, void* dk, void* dv, float* dg, float* dbeta, hipStream_t st);

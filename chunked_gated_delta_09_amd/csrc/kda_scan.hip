@@ -176,21 +176,6 @@ __global__ __launch_bounds__(64) void scan_kernel(Shape s, const T* __restrict__
 // transposes it, and the column choice makes the transposed values of two slices one
 // contiguous B fragment.
 
-// Global -> LDS copies (lane i's bytes land at lds + i * bytes). Issued as inline assembly:
-// the compiler's wait insertion would otherwise treat every LDS read of the ring as
-// depending on these copies and make the reading wave wait for all of its own outstanding
-// global stores. The copying wave waits for its copies explicitly (vmcnt) before the barrier
-// that hands them over.
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
-}
-__device__ __forceinline__ void copy16_to_lds(const void* g, const void* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory", "m0");
-}
-__device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory", "m0");
-}
-
 // Ring slot layout, in 1 KB blocks: P1 fragments, P2 fragments, e^gam, then either (WQ) the
 // Q'^T fragments (P2's layout) and the dO rows of the slices' 32-column groups (C rows x 64
 // bytes per group: the columns of slices 2m and 2m + 1 are the value columns 32m .. 32m + 31),
@@ -272,7 +257,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
         copy16_to_lds(p2 + 512 * b, slot + 1024 * (RG::NB1 + b));
       copy16_to_lds(eg + ch * K + 4 * (lane % (K / 4)), slot + 1024 * RG::OE);
       if constexpr (RG::WQ) {
-        const bf16* p3 = Ws + ch * K * V + 8 * lane;  // Q'^T in the W buffer
+        const bf16* p3 = Ws + ch * F::P2_ELEMS + 8 * lane;  // Q'^T in the W buffer
 #pragma unroll
         for (int b = 0; b < RG::NB3; ++b) copy16_to_lds(p3 + 512 * b, slot + 1024 * (RG::O3 + b));
         // dO rows of the chunk (rows past its end repeat its last row: Q' is zero there),

@@ -18,6 +18,8 @@
  *   kda_chunk_bwd  -- the chunkwise backward: given dO and optionally dS_final (the
  *                     gradient w.r.t. the final state) returns dq, dk, dv, dg, dbeta, dh0,
  *                     the vector-Jacobian product of sum<dO,o> + <dS_final,S_T>.
+ * kda_fwd_states_save / kda_chunk_bwd_saved are the same pair with the backward's chunk
+ * operands kept from the forward (saved-operand mode, below).
  *
  * Conventions shared by every call:
  *  - All tensor arguments are DEVICE pointers (the GPU of the current HIP device),
@@ -140,6 +142,45 @@ kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const void* k, con
                          const void* dO, const void* dS_final,
                          void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Saved-operand mode (FLA chunk_kda_bwd page: its disable_recompute switch, under which the
+ * backward takes the w, u and state tensors the forward kept instead of recomputing them):
+ * the forward also writes, per chunk, what kda_chunk_bwd's first kernel would otherwise
+ * recompute from q, k, g, beta and INV -- kr = k e^(gam - G), -w^T with
+ * w = INV diag(beta) (k e^G), Q'^T with Q' = qd - Mqk w, and e^gam -- and the backward
+ * reads them. Same results as kda_fwd_states + kda_chunk_bwd (up to fp32 rounding order in
+ * Q'); the backward no longer runs its prep kernel, the forward writes the extra tensors.
+ *
+ * kda_saved_bytes: size of the `saved` buffer (a caller-owned device buffer, 256-byte
+ * aligned; contents opaque, valid for the dims, inputs and states it was written with);
+ * 0 if dims are invalid.
+ */
+size_t kda_saved_bytes(const kda_dims* dims);
+
+/*
+ * kda_fwd_states that also fills `saved`. Arguments as kda_fwd_states, except that q and o
+ * are required (the save's Q' is formed beside o). Errors: KDA_EINVAL for a NULL, short or
+ * misaligned `saved`, or a NULL q or o (when the dims have at least one chunk).
+ */
+kda_status kda_fwd_states_save(const kda_dims* dims, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const void* h0,
+                               void* states, void* inv, float* final_state, void* o,
+                               void* saved, size_t saved_bytes,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * kda_chunk_bwd reading `saved` as written by kda_fwd_states_save for the same dims and
+ * inputs. Arguments and outputs as kda_chunk_bwd (same workspace size); q, k, g, beta and
+ * inv are still read by its gradient kernel. Errors as kda_chunk_bwd, plus KDA_EINVAL for a
+ * NULL, short or misaligned `saved`.
+ */
+kda_status kda_chunk_bwd_saved(const kda_dims* dims, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const void* states, const void* inv,
+                               const void* saved, size_t saved_bytes,
+                               const void* dO, const void* dS_final,
+                               void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                               void* workspace, size_t ws_bytes, void* stream);
 
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* kda_last_error(void);

@@ -32,17 +32,20 @@ def to_dev(t):
     return None if t is None else t.contiguous().cuda()
 
 
-def run_gpu(inp, C=None, output_o=True, beta_logits=False):
+def run_gpu(inp, C=None, output_o=True, beta_logits=False, saved=False):
+    """kda_fwd_states + kda_chunk_bwd on the GPU; ``saved``: the saved-operand pair
+    kda_fwd_states_save + kda_chunk_bwd_saved instead."""
     import chunked_gated_delta_09_amd as kda
     w = inp["workload"]
     C = w.C if C is None else C
     q, k, v, g, beta, h0, dsf, dO = (to_dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "h0", "dS_final", "dO"))
     f = kda.fwd_states(q, k, v, g, beta, h0=h0, cu_seqlens=inp["cu_seqlens"], C=C, scale=inp["scale"],
-                       output_o=output_o, beta_logits=beta_logits)
+                       output_o=output_o, beta_logits=beta_logits, save=saved)
     b = kda.chunk_bwd(q, k, v, g, beta, f["states"], f["inv"], dO, dS_final=dsf, cu_seqlens=inp["cu_seqlens"], C=C,
-                      scale=inp["scale"], beta_logits=beta_logits)
+                      scale=inp["scale"], beta_logits=beta_logits, saved=f["saved"])
     torch.cuda.synchronize()
-    out = {key: (val.float().cpu().numpy() if val is not None else None) for key, val in {**f, **b}.items()}
+    out = {key: (val.float().cpu().numpy() if val is not None else None) for key, val in {**f, **b}.items()
+           if key != "saved"}
     return out
 
 

@@ -118,6 +118,35 @@ def test_null_pointers_and_small_workspace(lib):
     assert "q (needed for o)" in lib.kda_last_error().decode()
 
 
+def test_saved_mode_validation(lib):
+    """The saved-operand entry points check their extra buffer (and the save's need for q and
+    o) before any HIP call."""
+    d, _ = _dims()
+    need = kda.saved_bytes(d)
+    # kr, -w^T, Q'^T in bf16 and e^gam in fp32 per chunk-head, 64 chunks x 8 heads
+    assert need >= 64 * 8 * (3 * 64 * 128 * 2 + 128 * 4)
+    p = ctypes.c_void_p(256)
+    big = 1 << 40
+    args = [p] * 7  # q, k, v, g, beta, states, inv
+    outs = [p, None, p, p, p, p, p, None]  # dO, dS_final, dq, dk, dv, dg, dbeta, dh0
+    assert lib.kda_chunk_bwd_saved(ctypes.byref(d), *args, None, need, *outs, p, big, None) == -1
+    assert "saved is NULL" in lib.kda_last_error().decode()
+    assert lib.kda_chunk_bwd_saved(ctypes.byref(d), *args, p, need - 1, *outs, p, big, None) == -1
+    assert "saved buffer too small" in lib.kda_last_error().decode()
+    assert lib.kda_chunk_bwd_saved(ctypes.byref(d), *args, ctypes.c_void_p(257), need, *outs, p, big, None) == -1
+    assert "256-byte aligned" in lib.kda_last_error().decode()
+    # forward: q and o required, then the buffer
+    fargs = [p, p, p, p, None, p, p, None]  # k, v, g, beta, h0, states, inv, final_state
+    assert lib.kda_fwd_states_save(ctypes.byref(d), p, *fargs, None, p, need, p, big, None) == -1
+    assert "o (the save" in lib.kda_last_error().decode()
+    assert lib.kda_fwd_states_save(ctypes.byref(d), None, *fargs, p, p, need, p, big, None) == -1
+    assert "q" in lib.kda_last_error().decode()
+    assert lib.kda_fwd_states_save(ctypes.byref(d), p, *fargs, p, p, 16, p, big, None) == -1
+    assert "saved buffer too small" in lib.kda_last_error().decode()
+    bad, _ = _dims(C=32)
+    assert kda.saved_bytes(bad) == 0
+
+
 def test_workload_table_is_consistent():
     for wid, w in kin.WORKLOADS.items():
         if w.varlen:

@@ -18,8 +18,9 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("save", [True, False], ids=["saved_operands", "recompute"])
 @pytest.mark.parametrize("name", list(CASES) + ["bf16_dense_logits"])
-def test_autograd_matches_oracle_and_direct_call(oracle_mod, name):
+def test_autograd_matches_oracle_and_direct_call(oracle_mod, name, save):
     from chunked_gated_delta_09_amd.autograd import kda_chunk
     logits = name.endswith("_logits")
     w, wid = CASES[name[:-len("_logits")] if logits else name]
@@ -34,7 +35,7 @@ def test_autograd_matches_oracle_and_direct_call(oracle_mod, name):
     leaf = {n: inp[n].contiguous().cuda().requires_grad_(True) for n in ("q", "k", "v", "g", "beta")}
     h0 = None if inp["h0"] is None else inp["h0"].contiguous().cuda().requires_grad_(True)
     o, fin = kda_chunk(leaf["q"], leaf["k"], leaf["v"], leaf["g"], leaf["beta"], h0=h0, cu_seqlens=inp["cu_seqlens"],
-                       C=w.C, scale=inp["scale"], beta_logits=logits)
+                       C=w.C, scale=inp["scale"], beta_logits=logits, save_operands=save)
     dO = inp["dO"].cuda().float()
     dsf = inp["dS_final"].cuda().float()
     loss = (o.float() * dO).sum() + (fin * dsf).sum()
@@ -56,11 +57,11 @@ def test_autograd_matches_oracle_and_direct_call(oracle_mod, name):
         got["dh0"] = h0.grad.float().cpu().numpy()
     tol = TOL[w.dtype]
     errs = {k: rel_l2(v, ref[k]) for k, v in got.items()}
-    print(f"[autograd {name}] " + " ".join(f"{k}={v:.2e}" for k, v in sorted(errs.items())), flush=True)
+    print(f"[autograd {name} save={save}] " + " ".join(f"{k}={v:.2e}" for k, v in sorted(errs.items())), flush=True)
     assert all(e <= tol for e in errs.values()), errs
 
     # the same kernels on the same inputs through the direct calls: identical gradients
-    direct = run_gpu(inp, beta_logits=logits)
+    direct = run_gpu(inp, beta_logits=logits, saved=save)
     for key in ("dq", "dk", "dv", "dg", "dbeta"):
         a = got[key].reshape(-1)
         b = direct[key].reshape(-1)
