@@ -191,7 +191,7 @@ def saved_read_bytes(w, inp):
     return num_chunks(w, inp) * w.HV * (3 * w.C * w.K * es + w.K * 4)
 
 
-def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True, saved=True):
+def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True, saved=True, recompute=True):
     """Times kda_chunk_bwd on workload `wid`: cold and (optionally) warm call times, and the
     per-kernel times from the library's event hook; optionally the forward with o, and the
     saved-operand pair (kda_fwd_states_save + kda_chunk_bwd_saved)."""
@@ -259,11 +259,14 @@ def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True, saved=T
             hip.destroy(kern_ev)
         return calls, kern, wall
 
-    for _ in range(warmup):
-        step()
     res = {"workload": w, "inp": inp}
-    res["cold_calls"], _, res["cold_wall"] = timed(steps, flush=True, per_kernel=False)
-    _, res["cold_kern"], _ = timed(steps, flush=True, per_kernel=True)
+    if not recompute:  # only the saved-operand pair (profiler runs of its kernels)
+        warm = forward = False
+    else:
+        for _ in range(warmup):
+            step()
+        res["cold_calls"], _, res["cold_wall"] = timed(steps, flush=True, per_kernel=False)
+        _, res["cold_kern"], _ = timed(steps, flush=True, per_kernel=True)
     if warm:
         res["warm_calls"], _, _ = timed(steps, flush=False, per_kernel=False)
         _, res["warm_kern"], _ = timed(steps, flush=False, per_kernel=True)
@@ -395,6 +398,11 @@ def main():
                     help="further workload ids measured under per_workload ('' for none)")
     ap.add_argument("--other-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-saved", action="store_true",
+                    help="skip the saved-operand pair (kda_fwd_states_save + kda_chunk_bwd_saved)")
+    ap.add_argument("--saved-only", action="store_true",
+                    help="time only the saved-operand pair on --workload and print its figures (for profiler "
+                         "runs of its kernels)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exit")
@@ -417,7 +425,13 @@ def main():
 
     hip = Hip()
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=torch.device("cuda:0"))
-    main_res = measure(args.workload, args.steps, args.warmup, hip, flush_buf)
+    if args.saved_only:
+        r = measure(args.workload, args.steps, args.warmup, hip, flush_buf, recompute=False)
+        print(json.dumps({"workload": r["workload"].name, "saved_bwd_ms_cold_median": statistics.median(r["saved_calls"]),
+                          "saved_bwd_kernels_ms_cold": {k: statistics.median(v) for k, v in r["saved_kern"].items()},
+                          "saved_fwd_ms_cold_median": statistics.median(r["saved_fwd_calls"])}), flush=True)
+        return
+    main_res = measure(args.workload, args.steps, args.warmup, hip, flush_buf, saved=not args.no_saved)
     s = summarize(main_res)
     w, inp = main_res["workload"], main_res["inp"]
     others = [int(x) for x in args.others.split(",") if x.strip()]
@@ -425,7 +439,7 @@ def main():
     for wid in others:
         if wid == args.workload:
             continue
-        r = measure(wid, args.other_steps, 2, hip, flush_buf, warm=False, forward=True)
+        r = measure(wid, args.other_steps, 2, hip, flush_buf, warm=False, forward=True, saved=not args.no_saved)
         per_workload[str(wid)] = summarize(r)
         del r
 
