@@ -69,3 +69,29 @@ def test_saved_full_workload_sampled_heads(oracle_mod, wid):
     errs, bad = compare(inp, out, ref, qk_heads=heads)
     _report(f"saved full w{wid}", errs)
     assert not bad, bad
+
+
+@pytest.mark.parametrize("channels", ["all", "upper_half"])
+def test_saved_strong_decay_c64(oracle_mod, channels):
+    """Saved-operand mode under per-token gates in [-5, -0.5] at C = 64 (chunk cumsums of -100
+    to -320): the saved kr, -w^T and Q' are formed from factors at most 1 (e^G, e^(gam - G))
+    and the sub-block-referenced Mqk, so every output stays finite and within the tolerance
+    per tensor (three times it per (chunk, head)), as in the recomputing path."""
+    from tests.kda_cases import TOL, small_workload
+    import torch
+    w = small_workload("strong_decay_c64", B=2, T=150, H=2, HV=4, C=64, has_h0=True, has_dsf=True)
+    inp = kin.make_inputs(w, seed=23)
+    gen = torch.Generator().manual_seed(24)
+    strong = -(0.5 + 4.5 * torch.rand(inp["g"].shape, generator=gen))
+    if channels == "all":
+        inp["g"] = strong
+    else:
+        inp["g"][..., 64:] = strong[..., 64:]
+    out = run_gpu(inp, saved=True)
+    for key in GRADS + ["o", "final_state"]:
+        assert out.get(key) is not None and np.isfinite(out[key]).all(), key
+    ref = run_oracle(oracle_mod, inp)
+    errs, bad = compare(inp, out, ref)
+    _report(f"saved strong decay C=64 {channels}", errs)
+    assert not {k: v for k, v in bad.items() if "@chunk" not in k}, bad
+    assert all(v <= 3 * TOL["bf16"] for k, v in errs.items() if "@chunk" in k), errs
