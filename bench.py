@@ -6,7 +6,10 @@ state-gradient scan, chunk gradients). Its inputs -- q, k, v, g, beta, dO, dS_fi
 per-chunk states and WY/UT inverses written beforehand by kda_fwd_states -- are resident in
 HBM before timing starts. Before every timed step a 1 GiB buffer is written so that neither
 L2 nor the 256 MB Infinity Cache holds the inputs (cold-cache timing); the flush itself is
-outside the timed interval, which HIP events bracket on the call's stream. Warm-cache
+outside the timed interval, which HIP events bracket on the call's stream. That flush leaves
+the caches full of dirty lines, which the call's reads then have to write back; `cold_clean`
+repeats the timing with a second 1 GiB buffer read after the write, so that the caches hold
+clean lines of neither input (the headline keeps the dirty-cache figure). Warm-cache
 (back-to-back) timing is reported alongside.
 
 Prints one JSON line. `value` is token-heads per second (tokens x value heads / median cold
@@ -191,10 +194,12 @@ def saved_read_bytes(w, inp):
     return num_chunks(w, inp) * w.HV * (3 * w.C * w.K * es + w.K * 4)
 
 
-def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True, saved=True, recompute=True):
+def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True, saved=True, recompute=True,
+            clean_buf=None):
     """Times kda_chunk_bwd on workload `wid`: cold and (optionally) warm call times, and the
-    per-kernel times from the library's event hook; optionally the forward with o, and the
-    saved-operand pair (kda_fwd_states_save + kda_chunk_bwd_saved)."""
+    per-kernel times from the library's event hook; with `clean_buf`, cold times again after a
+    flush that leaves clean lines (the write, then a read of clean_buf); optionally the forward
+    with o, and the saved-operand pair (kda_fwd_states_save + kda_chunk_bwd_saved)."""
     import torch
     import chunked_gated_delta_09_amd as kda
     from chunked_gated_delta_09_amd import inputs as kin
@@ -239,6 +244,8 @@ def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True, saved=T
         for i in range(nsteps):
             if flush:
                 flush_buf.fill_(i & 0xFF)
+            if flush == "clean":
+                clean_buf.max()
             if per_kernel:
                 kmeas.set_kernel_events(
                     ctypes.cast(ctypes.byref(kern_ev, 2 * nk * i * ctypes.sizeof(ctypes.c_void_p)),
@@ -267,6 +274,9 @@ def measure(wid, steps, warmup, hip, flush_buf, warm=True, forward=True, saved=T
             step()
         res["cold_calls"], _, res["cold_wall"] = timed(steps, flush=True, per_kernel=False)
         _, res["cold_kern"], _ = timed(steps, flush=True, per_kernel=True)
+        if clean_buf is not None:
+            res["clean_calls"], _, _ = timed(steps, flush="clean", per_kernel=False)
+            _, res["clean_kern"], _ = timed(steps, flush="clean", per_kernel=True)
     if warm:
         res["warm_calls"], _, _ = timed(steps, flush=False, per_kernel=False)
         _, res["warm_kern"], _ = timed(steps, flush=False, per_kernel=True)
@@ -355,6 +365,11 @@ def summarize(res):
     traffic = recorded_traffic(w.name)
     out["traffic"] = traffic  # rocprofv3 HBM bytes per call, or None (see recorded_traffic)
     out["traffic_over_algorithmic"] = None if traffic is None else traffic / abytes
+    if "clean_calls" in res:
+        cms = statistics.median(res["clean_calls"])
+        out["cold_clean"] = {"ms_median": cms, "token_heads_per_s": th / (cms * 1e-3),
+                             "call_frac": t_roof / (cms * 1e-3),
+                             "kernels_ms": {k: statistics.median(v) for k, v in res["clean_kern"].items()}}
     if "warm_calls" in res:
         out["ms_warm_median"] = statistics.median(res["warm_calls"])
         out["kernels_ms_warm"] = {k: statistics.median(v) for k, v in res["warm_kern"].items()}
@@ -425,13 +440,15 @@ def main():
 
     hip = Hip()
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=torch.device("cuda:0"))
+    clean_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=torch.device("cuda:0"))
     if args.saved_only:
         r = measure(args.workload, args.steps, args.warmup, hip, flush_buf, recompute=False)
         print(json.dumps({"workload": r["workload"].name, "saved_bwd_ms_cold_median": statistics.median(r["saved_calls"]),
                           "saved_bwd_kernels_ms_cold": {k: statistics.median(v) for k, v in r["saved_kern"].items()},
                           "saved_fwd_ms_cold_median": statistics.median(r["saved_fwd_calls"])}), flush=True)
         return
-    main_res = measure(args.workload, args.steps, args.warmup, hip, flush_buf, saved=not args.no_saved)
+    main_res = measure(args.workload, args.steps, args.warmup, hip, flush_buf, saved=not args.no_saved,
+                       clean_buf=clean_buf)
     s = summarize(main_res)
     w, inp = main_res["workload"], main_res["inp"]
     others = [int(x) for x in args.others.split(",") if x.strip()]
@@ -439,7 +456,8 @@ def main():
     for wid in others:
         if wid == args.workload:
             continue
-        r = measure(wid, args.other_steps, 2, hip, flush_buf, warm=False, forward=True, saved=not args.no_saved)
+        r = measure(wid, args.other_steps, 2, hip, flush_buf, warm=False, forward=True, saved=not args.no_saved,
+                    clean_buf=clean_buf)
         per_workload[str(wid)] = summarize(r)
         del r
 
@@ -484,6 +502,10 @@ def main():
                      "flops_frac_bf16": s["algorithmic_flops"] / (ms * 1e-3) / PEAK_BF16_FLOPS},
         "ms_per_step_p10_p50_p90_cold": [s["ms_cold_p10_p90"][0], ms, s["ms_cold_p10_p90"][1]],
         "ms_per_step_warm_median": s["ms_warm_median"],
+        # The same call after a flush that leaves the caches holding clean lines (1 GiB written,
+        # then another 1 GiB read): the headline's flush leaves them dirty, so its reads also
+        # wait for the flush's write-backs.
+        "cold_clean": dict(s["cold_clean"], flush="1 GiB written, then a second 1 GiB buffer read"),
         "kernels_ms_cold": s["kernels_ms_cold"],
         "kernels_ms_warm": s["kernels_ms_warm"],
         "forward": s["forward"],
