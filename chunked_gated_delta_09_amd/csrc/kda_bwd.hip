@@ -765,7 +765,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
               part[j] += dvc * to_f(vraw[it][jb][j]);
             }
             store_rows<T>(Ndv, LDV, 16 * mt, 16 * (nt0 + jb), ndv, lane, 1 << 30);
-            store_rows<T, true>(dvc_out, vs, 16 * mt, 16 * (nt0 + jb), dvb, lane, len);
+            store_rows<T>(dvc_out, vs, 16 * mt, 16 * (nt0 + jb), dvb, lane, len);
           }
           // row sums over the 16 columns; lane n < 4 writes row 4grp + n of the tile (each
           // block of a wave has its own row tile, so these are plain writes)
@@ -990,8 +990,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
             dbz[j] = kl * akd[rt][j];  // dbeta part 2: rowsum(kd o akd)
           }
           if constexpr (!GVA) {
-            store_rows<T, true>(dqc, qs, 16 * rt, 16 * kt, dq4, lane, len);
-            store_rows<T, true>(dkc, qs, 16 * rt, 16 * kt, dk4, lane, len);
+            store_rows<T>(dqc, qs, 16 * rt, 16 * kt, dq4, lane, len);
+            store_rows<T>(dkc, qs, 16 * rt, 16 * kt, dk4, lane, len);
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) dbz_sum[rt][j] += row_allsum16(dbz[j]);
@@ -1038,7 +1038,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
         for (int i = tid; i < SR * K / 4; i += NTH) {
           const int r = i / (K / 4), c4 = (i % (K / 4)) * 4;
           const int row = pass * SR + r;
-          // nontemporal, like the other gradient outputs (nothing later in the call reads it)
+          // nontemporal: nothing later in the call reads dg, and full rows leave as whole
+          // lines, so the marking keeps them from pushing the inputs that workgroups still
+          // to come will read out of the L2 and the Infinity Cache without adding traffic
+          // (the 8-byte row pieces of dq, dk and dv would leave as partial lines: plain
+          // stores, merged in L2, for those)
           if (row < len) __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(stg + r * LDG + c4), reinterpret_cast<f32x4*>(dgc + row * gs + c4));
         }
       }
@@ -1079,8 +1083,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
     if (kt < KT) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        store_rows<T, true>(dqc, qs, 16 * rt, 16 * kt, f32x4{dqa[ci][rt][0], dqa[ci][rt][1], dqa[ci][rt][2], dqa[ci][rt][3]}, lane, len);
-        store_rows<T, true>(dkc, qs, 16 * rt, 16 * kt, f32x4{dka[ci][rt][0], dka[ci][rt][1], dka[ci][rt][2], dka[ci][rt][3]}, lane, len);
+        store_rows<T>(dqc, qs, 16 * rt, 16 * kt, f32x4{dqa[ci][rt][0], dqa[ci][rt][1], dqa[ci][rt][2], dqa[ci][rt][3]}, lane, len);
+        store_rows<T>(dkc, qs, 16 * rt, 16 * kt, f32x4{dka[ci][rt][0], dka[ci][rt][1], dka[ci][rt][2], dka[ci][rt][3]}, lane, len);
       }
     }
   }

@@ -318,24 +318,13 @@ __device__ __forceinline__ f32x4 rows_to_cols_bf16(const short __attribute__((ex
 // Writes the 16 x 16 tile this wave holds in the column-owner layout (x[j]: row
 // r0 + 4(lane/16) + j, column c0 + lane%16) into a row-major array with row stride ld,
 // skipping rows >= rmax. bf16: transposed by to_rows_bf16, one 8-byte piece per lane
-// (row r0 + lane%16, columns c0 + 4(lane/16) ..); fp32: element by element. NT marks the
-// bf16 piece nontemporal: for outputs nothing later in the call reads, so that they do not
-// push still-needed inputs out of the L2 and the Infinity Cache. Whole-wave.
-template <class T, bool NT = false>
+// (row r0 + lane%16, columns c0 + 4(lane/16) ..); fp32: element by element. Whole-wave.
+template <class T>
 __device__ __forceinline__ void store_rows(T* __restrict__ base, int ld, int r0, int c0, f32x4 x, int lane, int rmax) {
   const int n = lane & 15, grp = lane >> 4;
   if constexpr (sizeof(T) == 2) {
     const f32x4 r = to_rows_bf16(x[0], x[1], x[2], x[3], lane);
-    if (r0 + n < rmax) {
-      T* dst = base + (r0 + n) * ld + c0 + 4 * grp;
-      if constexpr (NT) {
-        bf16x4 o;
-        o[0] = (bf16)r[0]; o[1] = (bf16)r[1]; o[2] = (bf16)r[2]; o[3] = (bf16)r[3];
-        __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
-      } else {
-        st4(dst, r);
-      }
-    }
+    if (r0 + n < rmax) st4(base + (r0 + n) * ld + c0 + 4 * grp, r);
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
