@@ -150,7 +150,9 @@ kda_status kda_chunk_bwd(const kda_dims* dims, const void* q, const void* k, con
  * recompute from q, k, g, beta and INV -- kr = k e^(gam - G), -w^T with
  * w = INV diag(beta) (k e^G), Q'^T with Q' = qd - Mqk w, and e^gam -- and the backward
  * reads them. Same results as kda_fwd_states + kda_chunk_bwd (up to fp32 rounding order in
- * Q'); the backward no longer runs its prep kernel, the forward writes the extra tensors.
+ * Q'); the backward no longer runs its prep kernel (where its reverse scan takes W = Q'^T dO
+ * precomputed, a smaller kernel forms W from the saved Q'^T), the forward writes the extra
+ * tensors (48.5 KB per chunk and value head at K = V = 128, C = 64).
  *
  * kda_saved_bytes: size of the `saved` buffer (a caller-owned device buffer, 256-byte
  * aligned; contents opaque, valid for the dims, inputs and states it was written with);
