@@ -2,7 +2,8 @@
 cotangents (dO, dS_final); packed sequences equal separate runs; grouped value heads equal
 the heads expanded with q and k replicated, then summed over each group. Each runs on the
 fp32 path (K = V = C = 16, tight tolerances) and the bf16 path (K = V = 128, C = 64,
-tolerances at bf16 rounding level)."""
+tolerances at bf16 rounding level), with the recomputing pair (kda_fwd_states +
+kda_chunk_bwd) and the saved-operand pair (kda_fwd_states_save + kda_chunk_bwd_saved)."""
 import numpy as np
 import pytest
 import torch
@@ -23,27 +24,29 @@ def _wl(name, path, **kw):
     return small_workload(name, **{**dims, **kw})
 
 
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
 @pytest.mark.parametrize("path", list(PATHS))
-def test_linear_in_cotangents(path):
+def test_linear_in_cotangents(path, saved):
     tol = PATHS[path][1]
     inp = kin.make_inputs(_wl("lin", path, B=2, T=90, H=1, HV=2, has_h0=True, has_dsf=True), seed=11)
     gen = torch.Generator().manual_seed(12)
     dO2 = torch.randn(inp["dO"].shape, generator=gen).to(inp["dO"].dtype)
     dsf2 = (0.1 * torch.randn(inp["dS_final"].shape, generator=gen)).to(inp["dS_final"].dtype)
-    a = run_gpu(inp, output_o=False)
-    b = run_gpu({**inp, "dO": dO2, "dS_final": dsf2}, output_o=False)
+    a = run_gpu(inp, output_o=False, saved=saved)
+    b = run_gpu({**inp, "dO": dO2, "dS_final": dsf2}, output_o=False, saved=saved)
     # 2 dO1 - dO2 is exact in bf16 only up to rounding; take it from the fp32 sum
     mix = {**inp, "dO": (2 * inp["dO"].float() - dO2.float()).to(inp["dO"].dtype),
            "dS_final": (2 * inp["dS_final"].float() - dsf2.float()).to(inp["dS_final"].dtype)}
-    c = run_gpu(mix, output_o=False)
+    c = run_gpu(mix, output_o=False, saved=saved)
     for key in GRADS:
         e = rel_l2(c[key], 2 * a[key].astype(np.float64) - b[key])
-        print(f"[linear {path}] {key} {e:.2e}", flush=True)
+        print(f"[linear {path} saved={saved}] {key} {e:.2e}", flush=True)
         assert e < tol, (key, e)
 
 
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
 @pytest.mark.parametrize("path", list(PATHS))
-def test_packed_equals_separate_runs(path):
+def test_packed_equals_separate_runs(path, saved):
     lens = [37, 70, 19] if path == "f32" else [150, 64, 97]
     cu = [0]
     for ln in lens:
@@ -52,7 +55,7 @@ def test_packed_equals_separate_runs(path):
             has_dsf=True)
     inp = kin.make_inputs(w, seed=13)
     inp["cu_seqlens"] = cu
-    packed = run_gpu(inp)
+    packed = run_gpu(inp, saved=saved)
     for n, (s0, s1) in enumerate(zip(cu[:-1], cu[1:])):
         one = {**inp, "B": 1, "T": s1 - s0, "N": 1, "cu_seqlens": None,
                "workload": _wl("one", path, B=1, T=s1 - s0, H=1, HV=2, has_h0=True, has_dsf=True)}
@@ -60,7 +63,7 @@ def test_packed_equals_separate_runs(path):
             one[key] = inp[key][:, s0:s1].contiguous()
         for key in ("h0", "dS_final"):
             one[key] = inp[key][n:n + 1].contiguous()
-        sep = run_gpu(one)
+        sep = run_gpu(one, saved=saved)
         for key in ("dq", "dk", "dv", "dg", "dbeta", "o"):
             e = rel_l2(packed[key][:, s0:s1], sep[key])
             assert e < 1e-6, (n, key, e)
@@ -69,27 +72,29 @@ def test_packed_equals_separate_runs(path):
             assert e < 1e-6, (n, key, e)
 
 
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
 @pytest.mark.parametrize("path", list(PATHS))
-def test_grouped_heads_equal_expanded_heads(path):
+def test_grouped_heads_equal_expanded_heads(path, saved):
     tol = PATHS[path][1]
     G = 3
     inp = kin.make_inputs(_wl("gva", path, B=1, T=80, H=1, HV=G, has_h0=True, has_dsf=True), seed=14)
-    grouped = run_gpu(inp)
+    grouped = run_gpu(inp, saved=saved)
     exp = {**inp, "workload": _wl("exp", path, B=1, T=80, H=G, HV=G, has_h0=True, has_dsf=True)}
     exp["q"] = inp["q"].repeat(1, 1, G, 1).contiguous()
     exp["k"] = inp["k"].repeat(1, 1, G, 1).contiguous()
-    expanded = run_gpu(exp)
+    expanded = run_gpu(exp, saved=saved)
     for key in ("dv", "dg", "dbeta", "dh0", "o", "final_state"):
         e = rel_l2(grouped[key], expanded[key])
         assert e < (1e-6 if key in ("o", "final_state") else tol), (key, e)
     for key in ("dq", "dk"):
         summed = expanded[key].astype(np.float64).sum(axis=2, keepdims=True)
         e = rel_l2(grouped[key], summed)
-        print(f"[gva {path}] {key} {e:.2e}", flush=True)
+        print(f"[gva {path} saved={saved}] {key} {e:.2e}", flush=True)
         assert e < tol, (key, e)
 
 
-def test_million_token_sequence_frozen_state():
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_million_token_sequence_frozen_state(saved):
     """Maximum-size case: one sequence of 2^20 tokens (16384 chunks per head) with g = 0 and
     beta = 0, where the state stays h0 and every output has a closed form (with
     P_t = dS_final + scale sum_{s>=t} q_s dO_s^T): o_t = scale h0^T q_t; dq_t = scale h0 dO_t;
@@ -100,8 +105,8 @@ def test_million_token_sequence_frozen_state():
     inp = kin.make_inputs(w, seed=15)
     inp["g"] = torch.zeros_like(inp["g"])
     inp["beta"] = torch.zeros_like(inp["beta"])
-    print("[frozen 1M] running GPU", flush=True)
-    out = run_gpu(inp)
+    print(f"[frozen 1M saved={saved}] running GPU", flush=True)
+    out = run_gpu(inp, saved=saved)
     assert np.abs(out["dk"]).max() == 0 and np.abs(out["dv"]).max() == 0
     scale = inp["scale"]
     for h in range(H):
@@ -124,6 +129,6 @@ def test_million_token_sequence_frozen_state():
         P = dsf[None] + scale * np.cumsum(np.einsum("tk,tv->tkv", q[t0:], dO[t0:])[::-1], axis=0)[::-1]
         resid = v[t0:] - k[t0:] @ h0
         errs["dbeta"] = rel_l2(out["dbeta"][0, t0:, h], np.einsum("tk,tkv,tv->t", k[t0:], P, resid))
-        print(f"[frozen 1M head {h}] " + " ".join(f"{key}={e:.2e}" for key, e in errs.items()), flush=True)
+        print(f"[frozen 1M saved={saved} head {h}] " + " ".join(f"{key}={e:.2e}" for key, e in errs.items()), flush=True)
         for key, e in errs.items():
             assert e < 2e-2, (h, key, e)
