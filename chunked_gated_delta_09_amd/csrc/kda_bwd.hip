@@ -523,8 +523,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(Shape s, const T* __restr
       const int blk = min(wave + it * NW, RT * (VT / BN1) - 1);
       const int mt = blk / (VT / BN1), nt0 = (blk % (VT / BN1)) * BN1;
 #pragma unroll
-      for (int jb = 0; jb < BN1; ++jb)
-        yraw[it][jb] = *reinterpret_cast<const t4*>(yT + (16 * (nt0 + jb) + n) * C + 16 * mt + 4 * grp);
+      for (int jb = 0; jb < BN1; ++jb) {
+        const int v = 16 * (nt0 + jb) + n;
+        if constexpr (sizeof(T) == 2)  // the bf16 scan's order: value column v at lane column lane_col(v) of slice slice(v)
+          yraw[it][jb] = *reinterpret_cast<const t4*>(yT + ScanFrag<K, V, C>::seed(ScanCols::slice(v), mt, RT, ScanCols::lane_col(v) + 16 * grp));
+        else
+          yraw[it][jb] = *reinterpret_cast<const t4*>(yT + v * C + 16 * mt + 4 * grp);
+      }
     }
     float gam[NCT];
     bool strong_c[NCT];  // column tile ci takes block references

@@ -48,7 +48,8 @@ struct BwdWs {
                //          chunk-head every ScanFrag::P2_ELEMS elements)
   float* eg;   // [K]      e^gam
   void* dS;    // [K][V]   gradient w.r.t. each chunk's S_out
-  void* yT;    // [V][C]   (kr dS)^T
+  void* yT;    // (kr dS)^T: bf16 in the reverse scan's lane-major order (tile m of slice vt at
+               //          ScanFrag::seed(vt, m, C/16, lane)), fp32 [V][C]
 };
 
 // Value slices (16 columns each) per workgroup of the bf16 scans: the fewest that keep the

@@ -456,8 +456,10 @@ __global__ __launch_bounds__(64 * (NC + 1)) void scan_bf16_kernel(Shape s, const
 #pragma unroll
       for (int m = 0; m < CT; ++m) Y[m] = M::mma(F1(m, p), bx[p], Y[m]);
     if constexpr (!FWD) {
+      // (kr dS)^T in the slices' lane-major order (64 lanes x 8 bytes per tile m, contiguous),
+      // as the gradient kernel reads it
 #pragma unroll
-      for (int m = 0; m < CT; ++m) st4(Yout + ch * V * C + vcol * C + 16 * m + 4 * grp, Y[m]);
+      for (int m = 0; m < CT; ++m) st4(Yout + ch * V * C + F::seed(vt, m, CT, lane), Y[m]);
     }
 
     // X = diag(e^gam) X + W + P2 Y, accumulated in place (X itself is no longer needed: Y
