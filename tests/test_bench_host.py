@@ -92,3 +92,34 @@ def test_forward_algorithmic_bytes():
     per_seq = w.HV * w.K * w.V * (2 + 4)
     assert per_th == 2180
     assert bench.fwd_algorithmic_bytes(w, inp) == round(th * per_th + inp["N"] * per_seq)
+
+
+def test_saved_read_bytes_is_the_librarys_save():
+    """The saved-operand backward's extra algorithmic bytes are the save it reads: kr, -w^T and
+    Q'^T (C x K bf16 each) and e^gam (K fp32) per chunk-head, 48.5 KB at K = 128, C = 64; the
+    library's own size query for the same dims agrees (its sub-buffers are 256-byte aligned,
+    which these sizes already are)."""
+    import chunked_gated_delta_09_amd as kda
+    bench = _bench()
+    for wid in (1, 4):
+        w = kin.WORKLOADS[wid]
+        inp = kin.make_inputs(w, wid=wid)
+        per_chunk_head = 3 * w.C * w.K * 2 + w.K * 4
+        assert per_chunk_head == 49664
+        assert bench.saved_read_bytes(w, inp) == bench.num_chunks(w, inp) * w.HV * per_chunk_head
+        dims, keep = kda.make_dims(inp["B"], inp["T"], w.H, w.HV, w.K, w.V, w.C, inp["scale"], w.dtype,
+                                   inp["cu_seqlens"])
+        assert kda.saved_bytes(dims) == bench.saved_read_bytes(w, inp)
+    assert bench.saved_read_bytes(kin.WORKLOADS[1], kin.make_inputs(kin.WORKLOADS[1], wid=1)) == 25427968
+
+
+def test_scan_forms_w_follows_the_slice_rule():
+    """The reverse scan forms W itself when a workgroup holds 4 or more of the 16-column value
+    slices (the fewest slices per workgroup that keep the grid near 256 workgroups): 16 (sequence,
+    head) pairs x 8 slices fit one per workgroup (workloads 1, 2), 256 pairs need 8 per workgroup
+    (the packed workload 3), 128 need 4 (workload 4); never on the fp32 path."""
+    bench = _bench()
+    expect = {0: False, 1: False, 2: False, 3: True, 4: True}
+    for wid, want in expect.items():
+        w = kin.WORKLOADS[wid]
+        assert bench.scan_forms_w(w, kin.make_inputs(w, wid=wid)) is want, wid
