@@ -2,8 +2,8 @@
 gradients as the recomputing pair, checked against the fp64 oracle to the parity tests'
 tolerances (relative L2 1e-4 fp32, 2e-2 bf16, per tensor and per (chunk, head) piece), on the
 small cases (both W paths of the reverse scan: seeds from the small W kernel, and W formed in
-the scan with 4-8 value slices per workgroup), two full-size workloads on sampled heads, and
-against the recomputing pair itself."""
+the scan with 4-8 value slices per workgroup), the four full-size workloads on sampled heads
+(the last q/k head among them), and against the recomputing pair itself."""
 import numpy as np
 import pytest
 
@@ -56,7 +56,7 @@ def test_saved_bitwise_determinism():
         assert np.array_equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("wid", [1, 4])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
 def test_saved_full_workload_sampled_heads(oracle_mod, wid):
     inp = kin.make_inputs(kin.WORKLOADS[wid], wid=wid)
     print(f"[saved full w{wid}] running GPU", flush=True)
